@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused 4-bit-weight GEMV/GEMM library on one MI355X.
+
+The timed step is one replay of the decode step's HIP graph: 48 layers x 7
+INT4 linears (q 3840->4096, k and v 3840->2048, o 4096->3840, gate and up
+3840->15360, down 15360->3840), group 128, FP16 scale and zero, BF16
+activations, M = 1, every linear reading its own static input.  Inputs are
+seeded synthetic data already resident in device memory.  ``value`` is the
+algorithmic bytes of one step (packed weights + scales + zeros + x + y, each
+once) divided by the measured time per step.
+
+Also reported, outside the timed step:
+  * ``roofline``: the dominant GEMV kernel's own achieved bandwidth, from HIP
+    events around each of its launches on the stream they run on;
+  * ``extra``: the single 3840 x 3840 GEMV, the 262144-row logits GEMV, the
+    two M = 128 prefill GEMMs (TFLOP/s) and the six-expert FP4 MoE pair,
+    each replayed over rotated weight copies so the data comes from HBM;
+  * ``cpu_baseline``: the FP64 oracle timed on host cores on a sample of the
+    same step.
+
+    python bench.py [--steps K] [--warmup W] [--no-extra] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import pathlib
+import sys
+import time
+
+ROOT = pathlib.Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "M=1 W4A16 GEMV achieved HBM GB/s (% of peak) + µs/decode-step; M=128 TFLOP/s"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the FP64 oracle")
+    p.add_argument("--cpu-layers", type=int, default=1, help="decode layers the oracle sample covers")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------ helpers
+def make_decode_step(w4, host, si, torch):
+    from gemm_w4_gemv_amd.decode import DecodeStep
+
+    lins = []
+    for layer, idx, name, K, N in si.decode_step_specs():
+        lin_np, x_bits = si.decode_linear(layer, idx)
+        t = host.int4_tensors(lin_np)
+        t["x"] = host.bf16_tensor(x_bits)
+        t["y"] = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+        t["name"], t["K"], t["N"] = name, K, N
+        lins.append(t)
+    torch.cuda.synchronize()
+    return DecodeStep(lins)
+
+
+def time_graph(torch, replay, stream, reps: int, warmup: int = 2):
+    """Milliseconds per replay, from HIP events on ``stream`` around ``reps`` replays."""
+    for _ in range(warmup):
+        replay()
+    stream.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        replay()
+    b.record(stream)
+    b.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def capture(w4, torch, stream, body):
+    torch.cuda.synchronize()
+    w4.w4_graph_begin(stream)
+    try:
+        body()
+    finally:
+        g = w4.w4_graph_end(stream)
+    return g
+
+
+def per_launch_durations(w4, torch, step):
+    """Eager pass of the step with an event pair around every launch (same stream)."""
+    stream = step.stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in step.linears]
+    torch.cuda.synchronize()
+    for (a, b), lin in zip(evs, step.linears):
+        a.record(stream)
+        w4.w4_gemv(lin["x"], lin["qw"], lin["s"], lin["z"], lin["y"], stream=stream)
+        b.record(stream)
+    stream.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in evs]  # microseconds
+
+
+def extra_workloads(w4, host, si, torch, rf):
+    """Other workloads, each as a graph over rotated weight copies (>= 512 MB walked)."""
+    out = {}
+    stream = torch.cuda.Stream()
+    MB = 1 << 20
+
+    # single 3840 x 3840 GEMV
+    K, N = 3840, 3840
+    copies = []
+    per = rf.int4_weight_bytes(K, N)
+    n_copies = -(-(512 * MB) // per) + 1
+    for c in range(n_copies):
+        lin = si.int4_linear(100, (c,), K, N)
+        t = host.int4_tensors(lin)
+        copies.append(t)
+    x = host.bf16_tensor(si.bf16_normal(100, (9,), (K,)))
+    y = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+    g = capture(w4, torch, stream, lambda: [w4.w4_gemv(x, t["qw"], t["s"], t["z"], y, stream=stream) for t in copies])
+    ms = time_graph(torch, lambda: g.replay(stream), stream, reps=20)
+    us = ms * 1e3 / n_copies
+    gbps = rf.int4_linear_bytes(K, N) / (us * 1e-6) / 1e9
+    out["single_gemv_3840x3840"] = {"us_per_call": round(us, 3), "GBps": round(gbps, 1),
+                                    "frac_hbm": round(gbps / rf.HBM_PEAK_GBPS, 4), "copies": n_copies}
+    g.destroy()
+    del copies
+    log(f"single GEMV 3840x3840: {us:.2f} us, {gbps:.0f} GB/s")
+
+    # logits GEMV 3840 -> 262144
+    K, N = si.LOGITS_SHAPE
+    copies = [host.int4_tensors(si.int4_linear(101, (c,), K, N)) for c in range(2)]
+    x = host.bf16_tensor(si.bf16_normal(101, (9,), (K,)))
+    y = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+    g = capture(w4, torch, stream, lambda: [w4.w4_gemv(x, t["qw"], t["s"], t["z"], y, stream=stream) for t in copies])
+    ms = time_graph(torch, lambda: g.replay(stream), stream, reps=20)
+    us = ms * 1e3 / 2
+    gbps = rf.int4_linear_bytes(K, N) / (us * 1e-6) / 1e9
+    out["logits_gemv_3840x262144"] = {"us_per_call": round(us, 2), "GBps": round(gbps, 1),
+                                      "frac_hbm": round(gbps / rf.HBM_PEAK_GBPS, 4)}
+    g.destroy()
+    del copies
+    log(f"logits GEMV: {us:.1f} us, {gbps:.0f} GB/s")
+
+    # prefill M = 128
+    M = si.PREFILL_M
+    for si_idx, (K, N) in enumerate(si.PREFILL_SHAPES):
+        per = rf.int4_weight_bytes(K, N)
+        n_copies = -(-(512 * MB) // per) + 1
+        copies = [host.int4_tensors(si.int4_linear(102 + si_idx, (c,), K, N)) for c in range(n_copies)]
+        x = host.bf16_tensor(si.bf16_normal(102 + si_idx, (9,), (M, K)))
+        y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        nbytes = w4.w4_gemm_workspace_bytes(M, K, N)
+        ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device="cuda") if nbytes else None
+        g = capture(w4, torch, stream,
+                    lambda: [w4.w4_gemm(x, t["qw"], t["s"], t["z"], y, workspace=ws, stream=stream) for t in copies])
+        ms = time_graph(torch, lambda: g.replay(stream), stream, reps=10)
+        us = ms * 1e3 / n_copies
+        tf = rf.flops(M, K, N) / (us * 1e-6) / 1e12
+        out[f"prefill_m128_k{K}_n{N}"] = {"us_per_call": round(us, 2), "TFLOPs": round(tf, 1),
+                                          "frac_mfma_bf16": round(tf / rf.MFMA_BF16_PEAK_TFLOPS, 4),
+                                          "split_k_workspace_bytes": nbytes}
+        g.destroy()
+        del copies
+        log(f"prefill M=128 K={K} N={N}: {us:.1f} us, {tf:.0f} TFLOP/s")
+
+    # FP4 MoE: FC1 (shared x) then FC2 (one x per slot), a fresh id set per token
+    pools = [host.fp4_tensors(p) for p in si.moe_pools()]
+    tokens = 64
+    ids = torch.from_numpy(__import__("numpy").stack([si.moe_inputs(t)[0] for t in range(tokens)])).to("cuda")
+    _, x1b, x2b = si.moe_inputs(0)
+    x1, x2 = host.bf16_tensor(x1b), host.bf16_tensor(x2b)
+    (K1, N1), (K2, N2) = si.MOE_FC
+    y1 = torch.empty(si.MOE_SLOTS, N1, dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty(si.MOE_SLOTS, N2, dtype=torch.bfloat16, device="cuda")
+
+    def moe_tokens():
+        for t in range(tokens):
+            w4.w4_moe_gemv(x1, pools[0]["qw"], pools[0]["s"], ids[t], y1, stream=stream)
+            w4.w4_moe_gemv(x2, pools[1]["qw"], pools[1]["s"], ids[t], y2, stream=stream)
+
+    g = capture(w4, torch, stream, moe_tokens)
+    ms = time_graph(torch, lambda: g.replay(stream), stream, reps=10)
+    us = ms * 1e3 / tokens
+    nb = rf.moe_bytes(si.MOE_SLOTS, K1, N1, True) + rf.moe_bytes(si.MOE_SLOTS, K2, N2, False)
+    gbps = nb / (us * 1e-6) / 1e9
+    out["moe_fp4_6x2fc"] = {"us_per_token": round(us, 2), "GBps": round(gbps, 1),
+                            "frac_hbm": round(gbps / rf.HBM_PEAK_GBPS, 4), "bytes_per_token": nb}
+    g.destroy()
+    log(f"FP4 MoE 6 experts x 2 FC: {us:.1f} us/token, {gbps:.0f} GB/s")
+    return out
+
+
+def cpu_baseline(si, rf, layers: int):
+    """The FP64 oracle (as it stands) on the first ``layers`` decode layers: GB/s of algorithmic bytes."""
+    import numpy as np
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the process affinity
+        blas_threads = len(os.sched_getaffinity(0))
+    inputs = [si.decode_linear(layer, idx) for layer in range(layers) for idx in range(len(si.DECODE_LAYER))]
+    nbytes = sum(rf.int4_linear_bytes(lin["qw"].shape[1] * 8, lin["qw"].shape[0]) for lin, _ in inputs)
+    t0 = time.perf_counter()
+    for lin, x in inputs:
+        y = oracle.gemv_int4(x, lin["qw"], lin["s"], lin["z"])
+        assert np.all(np.isfinite(y))
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"decode layers 0..{layers - 1}: {len(inputs)} linears, {nbytes} algorithmic bytes, "
+                      f"{dt:.1f} s (FP64 numpy unpack + dequant + matmul)",
+            "seconds": round(dt, 2)}
+
+
+# --------------------------------------------------------------------- main
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the decode GEMV path is single-GPU here "
+              "(row sharding across GPUs is a design note, not built); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not (ROOT / "gemm_w4_gemv_amd" / "libw4.so").exists():
+        import __graft_entry__
+        __graft_entry__.build()
+    import gemm_w4_gemv_amd as w4
+    import seeded_inputs as si
+    from gemm_w4_gemv_amd import host
+    from gemm_w4_gemv_amd import roofline as rf
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+
+    log("generating and uploading the decode step (336 INT4 linears)")
+    step = make_decode_step(w4, host, si, torch)
+    step_bytes = sum(rf.int4_linear_bytes(l["K"], l["N"]) for l in step.linears)
+    step_flops = sum(rf.flops(1, l["K"], l["N"]) for l in step.linears)
+    step.capture()
+    log("graph captured; warm-up")
+
+    for _ in range(args.warmup):
+        step.replay()
+    torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(step.stream)
+    for _ in range(args.steps):
+        step.replay()
+    ev1.record(step.stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    gpu_ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"decode step: {ms_per_step * 1e3:.1f} us/step (events {gpu_ms_per_step * 1e3:.1f} us), {value:.0f} GB/s")
+
+    # roofline of the dominant kernel: per-launch events in an eager pass of the same launches
+    durs = per_launch_durations(w4, torch, step)
+    by_shape = {}
+    for lin, d in zip(step.linears, durs):
+        key = (lin["K"], lin["N"])
+        e = by_shape.setdefault(key, {"names": set(), "us": [], "bytes": rf.int4_linear_bytes(*key)})
+        e["names"].add(lin["name"])
+        e["us"].append(d)
+    dom_key = max(by_shape, key=lambda k: sum(by_shape[k]["us"]))
+    dom = by_shape[dom_key]
+    avg_us = sum(dom["us"]) / len(dom["us"])
+    achieved = dom["bytes"] / (avg_us * 1e-6) / 1e9
+    shapes = {f"{'/'.join(sorted(v['names']))} K{k[0]}->N{k[1]}":
+              {"launches": len(v["us"]), "avg_us": round(sum(v["us"]) / len(v["us"]), 3),
+               "GBps": round(v["bytes"] / (sum(v["us"]) / len(v["us"]) * 1e-6) / 1e9, 1)}
+              for k, v in by_shape.items()}
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / rf.HBM_PEAK_GBPS, 4), "traffic": None,
+                "kernel": f"gemv_int4 ({'/'.join(sorted(dom['names']))} projection, K{dom_key[0]}->N{dom_key[1]})",
+                "bytes_per_launch": dom["bytes"], "avg_launch_us": round(avg_us, 3),
+                "launches_timed": len(dom["us"]), "per_shape": shapes}
+    log(f"dominant kernel {roofline['kernel']}: {avg_us:.2f} us/launch, {achieved:.0f} GB/s")
+
+    extra = {}
+    if not args.no_extra:
+        extra = extra_workloads(w4, host, si, torch, rf)
+    step.destroy()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"timing the FP64 oracle on {args.cpu_layers} decode layer(s)")
+        cpu = cpu_baseline(si, rf, args.cpu_layers)
+        log(f"oracle: {cpu['value']} GB/s on {cpu['cores']} threads ({cpu['seconds']} s)")
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode step: one hipGraph replay of 48 layers x 7 INT4 GEMVs "
+                               "(q,k,v,o,gate,up,down; hidden 3840; group 128; M=1)",
+                   "linears": len(step.linears), "bytes_per_step": step_bytes, "flops_per_step": step_flops,
+                   "us_per_step": round(ms_per_step * 1e3, 1), "gpu_us_per_step": round(gpu_ms_per_step * 1e3, 1),
+                   "frac_hbm": round(value / rf.HBM_PEAK_GBPS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

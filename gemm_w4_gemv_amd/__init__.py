@@ -1,0 +1,257 @@
+"""Python binding of ``libw4.so``, the fused 4-bit-weight x BF16 GEMV/GEMM library.
+
+Argument marshalling only: each function takes torch tensors that already
+live in device memory, checks their dtypes and shapes, and passes raw
+pointers, sizes and the current HIP stream to the C entry point of the same
+name (declared in ``include/w4.h``).  Every step of the computation runs in
+the library's HIP kernels; there is no fallback.  If the shared library is
+not built, importing this package raises ImportError.
+
+Tensor formats (see ``include/w4.h``):
+    x     bfloat16 [M, K] (or [K])       qw      int32 [N, K/8]
+    s, z  float16  [N, K/128]            qw_fp4  uint8 [experts, N, K/2]
+    s_fp4 bfloat16 [experts, N, K/32]    y       bfloat16 [M, N] (or [N])
+"""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+
+import torch
+
+__all__ = [
+    "W4Error", "lib", "LIB_PATH", "w4_abi_version", "w4_status_string", "w4_last_error",
+    "w4_gemv", "w4_gemm", "w4_gemm_workspace_bytes", "w4_moe_gemv",
+    "w4_graph_begin", "w4_graph_end", "w4_graph_replay", "w4_graph_destroy", "W4Graph",
+    "w4_dequant_int4", "w4_dequant_fp4", "INT4_GROUP", "FP4_GROUP", "GEMV_MAX_K",
+]
+
+LIB_PATH = pathlib.Path(__file__).resolve().with_name("libw4.so")
+INT4_GROUP = 128
+FP4_GROUP = 32
+GEMV_MAX_K = 32768
+
+STATUS = {0: "W4_OK", 1: "W4_ERR_NULL", 2: "W4_ERR_SHAPE", 3: "W4_ERR_UNSUPPORTED", 4: "W4_ERR_ALIGN",
+          5: "W4_ERR_WORKSPACE", 6: "W4_ERR_ALIAS", 7: "W4_ERR_ARG", 8: "W4_ERR_HIP"}
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes), mirroring include/w4.h
+SIGNATURES = {
+    "w4_abi_version": (_i32, []),
+    "w4_status_string": (ctypes.c_char_p, [_i32]),
+    "w4_last_error": (ctypes.c_char_p, []),
+    "w4_gemv": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
+    "w4_gemm_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "w4_gemm": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "w4_moe_gemv": (_i32, [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "w4_graph_begin": (_i32, [_vp]),
+    "w4_graph_end": (_i32, [_vp, ctypes.POINTER(_vp)]),
+    "w4_graph_replay": (_i32, [_vp, _vp]),
+    "w4_graph_destroy": (None, [_vp]),
+    "w4_dequant_int4": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
+    "w4_dequant_fp4": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _vp]),
+}
+
+
+def _load() -> ctypes.CDLL:
+    if not LIB_PATH.exists():
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m gemm_w4_gemv_amd.build` "
+                          "(or __graft_entry__.build()) first")
+    handle = ctypes.CDLL(str(LIB_PATH))
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
+lib = _load()
+
+
+class W4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        self.name = STATUS.get(status, f"status {status}")
+        detail = lib.w4_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {self.name}: {detail}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise W4Error(status, where)
+
+
+def w4_abi_version() -> int:
+    return lib.w4_abi_version()
+
+
+def w4_status_string(status: int) -> str:
+    return lib.w4_status_string(status).decode()
+
+
+def w4_last_error() -> str:
+    return lib.w4_last_error().decode(errors="replace")
+
+
+# ---------------------------------------------------------------- marshalling
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtypes) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+_BF16 = (torch.bfloat16,)
+_F16 = (torch.float16,)
+_I32 = (torch.int32,)
+_U8 = (torch.uint8,)
+
+
+def _int4_weight(qw, s, z, K, group):
+    N = qw.shape[0]
+    if qw.dim() != 2 or qw.shape[1] * 8 != K:
+        raise ValueError(f"qw must be int32 [N, K/8] with K = {K}; got {tuple(qw.shape)}")
+    G = K // group if group > 0 else 0
+    for name, t in (("s", s), ("z", z)):
+        if tuple(t.shape) != (N, G):
+            raise ValueError(f"{name} must be [N, K/{group}] = {(N, G)}; got {tuple(t.shape)}")
+    return N, _dev(qw, "qw", _I32), _dev(s, "s", _F16), _dev(z, "z", _F16)
+
+
+def w4_gemv(x, qw, s, z, y, group: int = INT4_GROUP, stream=None) -> torch.Tensor:
+    """``y[n] = bf16(sum_k (q - z) s x)`` for one BF16 vector ``x [K]`` (M = 1)."""
+    K = x.numel()
+    N, pq, ps, pz = _int4_weight(qw, s, z, K, group)
+    if y.numel() != N:
+        raise ValueError(f"y must hold N = {N} values; got {tuple(y.shape)}")
+    _check(lib.w4_gemv(_dev(x, "x", _BF16), pq, ps, pz, _dev(y, "y", _BF16), K, N, group, _stream(stream)),
+           "w4_gemv")
+    return y
+
+
+def w4_gemm_workspace_bytes(M: int, K: int, N: int, group: int = INT4_GROUP) -> int:
+    return lib.w4_gemm_workspace_bytes(M, K, N, group)
+
+
+def w4_gemm(x, qw, s, z, y, workspace=None, group: int = INT4_GROUP, stream=None) -> torch.Tensor:
+    """``y [M, N] = x [M, K] @ bf16(dequant(W)).T`` with FP32 accumulation."""
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    N, pq, ps, pz = _int4_weight(qw, s, z, K, group)
+    if tuple(y.shape) != (M, N):
+        raise ValueError(f"y must be [M, N] = {(M, N)}; got {tuple(y.shape)}")
+    if workspace is None:
+        pw, nbytes = None, 0
+    else:
+        pw, nbytes = _dev(workspace, "workspace", (workspace.dtype,)), workspace.numel() * workspace.element_size()
+    _check(lib.w4_gemm(_dev(x, "x", _BF16), pq, ps, pz, _dev(y, "y", _BF16), M, K, N, group, pw, nbytes,
+                       _stream(stream)), "w4_gemm")
+    return y
+
+
+def w4_moe_gemv(x, qw_fp4, s_fp4, expert_ids, y, stream=None) -> torch.Tensor:
+    """Slot ``e`` applies FP4 expert ``expert_ids[e]`` to ``x`` ([K], shared) or ``x[e]`` ([E, K])."""
+    if qw_fp4.dim() != 3:
+        raise ValueError("qw_fp4 must be [experts, N, K/2]")
+    num_experts, N, half_k = qw_fp4.shape
+    K = 2 * half_k
+    if tuple(s_fp4.shape) != (num_experts, N, K // FP4_GROUP):
+        raise ValueError(f"s_fp4 must be [experts, N, K/32]; got {tuple(s_fp4.shape)}")
+    E = expert_ids.numel()
+    if x.dim() == 1:
+        stride = 0
+        if x.numel() != K:
+            raise ValueError(f"x must have K = {K} values")
+    else:
+        if x.dim() != 2 or x.shape[1] != K or x.shape[0] < E:
+            raise ValueError(f"x must be [E, K] = {(E, K)}; got {tuple(x.shape)}")
+        stride = K
+    if tuple(y.shape) != (E, N):
+        raise ValueError(f"y must be [E, N] = {(E, N)}; got {tuple(y.shape)}")
+    _check(lib.w4_moe_gemv(_dev(x, "x", _BF16), stride, _dev(qw_fp4, "qw_fp4", _U8), _dev(s_fp4, "s_fp4", _BF16),
+                           _dev(expert_ids, "expert_ids", _I32), _dev(y, "y", _BF16), E, num_experts, K, N,
+                           _stream(stream)), "w4_moe_gemv")
+    return y
+
+
+class W4Graph:
+    """An instantiated HIP graph owned by the library (w4_graph_t)."""
+
+    def __init__(self, handle: int):
+        self.handle = handle
+
+    def replay(self, stream=None) -> None:
+        w4_graph_replay(self, stream)
+
+    def destroy(self) -> None:
+        if self.handle:
+            lib.w4_graph_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def w4_graph_begin(stream) -> None:
+    _check(lib.w4_graph_begin(_stream(stream)), "w4_graph_begin")
+
+
+def w4_graph_end(stream) -> W4Graph:
+    h = _vp()
+    _check(lib.w4_graph_end(_stream(stream), ctypes.byref(h)), "w4_graph_end")
+    return W4Graph(h.value)
+
+
+def w4_graph_replay(graph: W4Graph, stream=None) -> None:
+    _check(lib.w4_graph_replay(graph.handle, _stream(stream)), "w4_graph_replay")
+
+
+def w4_graph_destroy(graph: W4Graph) -> None:
+    graph.destroy()
+
+
+def w4_dequant_int4(qw, s, z, out_f32=None, out_bf16=None, group: int = INT4_GROUP, stream=None) -> None:
+    """Test-only: FP32 and/or BF16 image of an INT4 weight, from the GEMM's unpack code."""
+    N, K = qw.shape[0], qw.shape[1] * 8
+    _, pq, ps, pz = _int4_weight(qw, s, z, K, group)
+    pf = _dev(out_f32, "out_f32", (torch.float32,)) if out_f32 is not None else None
+    pb = _dev(out_bf16, "out_bf16", _BF16) if out_bf16 is not None else None
+    for t in (out_f32, out_bf16):
+        if t is not None and tuple(t.shape) != (N, K):
+            raise ValueError(f"outputs must be [N, K] = {(N, K)}")
+    _check(lib.w4_dequant_int4(pq, ps, pz, pf, pb, K, N, group, _stream(stream)), "w4_dequant_int4")
+
+
+def w4_dequant_fp4(qw_fp4, s_fp4, out_f32=None, out_bf16=None, stream=None) -> None:
+    """Test-only: FP32 and/or BF16 image of one FP4 expert ``[N, K/2]``, from the GEMV's unpack code."""
+    N, K = qw_fp4.shape[0], qw_fp4.shape[1] * 2
+    if tuple(s_fp4.shape) != (N, K // FP4_GROUP):
+        raise ValueError("s_fp4 must be [N, K/32]")
+    pf = _dev(out_f32, "out_f32", (torch.float32,)) if out_f32 is not None else None
+    pb = _dev(out_bf16, "out_bf16", _BF16) if out_bf16 is not None else None
+    for t in (out_f32, out_bf16):
+        if t is not None and tuple(t.shape) != (N, K):
+            raise ValueError(f"outputs must be [N, K] = {(N, K)}")
+    _check(lib.w4_dequant_fp4(_dev(qw_fp4, "qw_fp4", _U8), _dev(s_fp4, "s_fp4", _BF16), pf, pb, K, N,
+                              _stream(stream)), "w4_dequant_fp4")

@@ -1,0 +1,85 @@
+"""Compile the HIP sources under ``csrc/`` into ``libw4.so`` (gfx950 only).
+
+Each ``.hip`` file is compiled to an object under ``_build/`` in parallel,
+then linked into ``gemm_w4_gemv_amd/libw4.so``, next to this file.  No GPU is
+needed: hipcc cross-compiles for gfx950.
+
+    python -m gemm_w4_gemv_amd.build            # build
+    python -m gemm_w4_gemv_amd.build --asm      # also write device assembly (.s)
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import pathlib
+import shutil
+import subprocess
+import sys
+
+PKG = pathlib.Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+BUILD = ROOT / "_build"
+LIB = PKG / "libw4.so"
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and pathlib.Path(cand).exists():
+            return cand
+    raise RuntimeError("hipcc not found (expected /opt/rocm/bin/hipcc)")
+
+
+def flags(extra=()) -> list[str]:
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+        f"-I{ROOT / 'include'}", f"-I{CSRC}",
+        # no packed-FP32 instructions anywhere in the device code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-command-line-argument",
+        *extra,
+    ]
+
+
+def _run(cmd):
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    out = (res.stdout + res.stderr).strip()
+    # the host pass does not know the device-only feature above; that note is harmless
+    lines = [ln for ln in out.splitlines() if "packed-fp32-ops" not in ln]
+    return res.returncode, "\n".join(lines)
+
+
+def build(verbose: bool = False, asm: bool = False, defines=()) -> pathlib.Path:
+    BUILD.mkdir(exist_ok=True)
+    cc = hipcc()
+    extra = [f"-D{d}" for d in defines]
+    sources = sorted(CSRC.glob("*.hip"))
+    jobs = []
+    for src in sources:
+        obj = BUILD / (src.stem + ".o")
+        jobs.append(([cc, *flags(extra), "-c", str(src), "-o", str(obj)], obj))
+        if asm:
+            jobs.append(([cc, *flags(extra), "--cuda-device-only", "-S", str(src),
+                          "-o", str(BUILD / (src.stem + ".s"))], None))
+    workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        results = list(ex.map(lambda j: (_run(j[0]), j[0]), jobs))
+    for (rc, out), cmd in results:
+        if out and (verbose or rc):
+            print(out, file=sys.stderr)
+        if rc:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}")
+    objs = [str(o) for _, o in jobs if o is not None]
+    tmp = LIB.with_suffix(".so.tmp")
+    rc, out = _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *objs])
+    if rc:
+        print(out, file=sys.stderr)
+        raise RuntimeError("link failed")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    path = build(verbose=True, asm="--asm" in sys.argv)
+    print(path)

@@ -1,0 +1,207 @@
+// Decode GEMV (M = 1) over packed INT4 weights with an FP16 scale and zero per
+// 128 along K.
+//
+// "Lab 5: Gemma4 端到端推理优化", section "INT4 融合 GEMV": the decode linear
+// sees a [1, hidden] input; the fused kernel reads the packed weights once,
+// unpacks them in registers, applies scale and zero per group and dots with
+// the input vector, keeping that vector in registers or shared memory.
+//
+// gfx950 design.  The kernel is bound by HBM: every weight byte is read once
+// with 16-byte (dwordx4) loads and nothing else of size is touched.
+//   * A row of K codes is C = K / 32 chunks of 16 bytes.  Lane l of a wave
+//     owns chunks l, l + 64, ... of its K-slice, so each load instruction of
+//     a wave reads 1 KiB of consecutive memory, and the lane's part of x
+//     never changes: it is loaded once and kept in registers as bf16 pairs.
+//   * Unpacking uses the bf16 bias trick: 0x4300 | q is the bf16 value
+//     128 + q, and one mask pulls two nibbles 16 bits apart, so a word of 8
+//     codes becomes 4 bf16 pairs in 7 integer operations, and
+//     v_dot2_f32_bf16 multiplies and adds two codes per instruction.
+//   * Scale and zero enter once per 32-code chunk (a chunk lies in one
+//     group): sum_k (q - z) s x = s (sum_k (128 + q) x - (128 + z) sum_k x),
+//     where sum_k x per chunk is precomputed with the x registers.
+//   * Each wave carries RPT rows at once (RPT x CPL loads in flight per
+//     lane), reduces them across lanes with a halving exchange, and the
+//     waves that split one row (long K) combine through LDS in a fixed
+//     order.  No atomics: results are bit-reproducible.
+#include "w4_device.hpp"
+#include "w4_internal.hpp"
+
+#ifndef W4_GEMV_MIN_BLOCKS
+#define W4_GEMV_MIN_BLOCKS 1024  // launch at least this many workgroups when N allows
+#endif
+
+namespace w4 {
+namespace {
+
+constexpr int kThreads = 256;
+
+// x pairs for one chunk, matching int4_word_biased_pairs, and their FP32 sum.
+// ``raw`` holds the chunk's 32 bf16 values x[32c .. 32c + 31] as loaded.
+__device__ __forceinline__ float x_chunk_pairs(const u32x4_t raw[4], uint32_t xp[16]) {
+    float sum = 0.f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t xw[4] = {raw[p].x, raw[p].y, raw[p].z, raw[p].w};
+        x_pairs_for_biased(xw, &xp[4 * p]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum += bf16_to_f32(xw[i] & 0xFFFFu) + bf16_to_f32(xw[i] >> 16);
+    }
+    return sum;
+}
+
+// sum over the chunk's 32 codes of (128 + q) * x.
+__device__ __forceinline__ float chunk_dot(const u32x4_t w, const uint32_t xp[16], uint32_t bias) {
+    const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+    float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        uint32_t t[4];
+        int4_word_biased_pairs(words[p], bias, t);
+        d0 = dot2_bf16(t[0], xp[4 * p + 0], d0);
+        d1 = dot2_bf16(t[1], xp[4 * p + 1], d1);
+        d0 = dot2_bf16(t[2], xp[4 * p + 2], d0);
+        d1 = dot2_bf16(t[3], xp[4 * p + 3], d1);
+    }
+    return d0 + d1;
+}
+
+// All loads are issued before any of their results is used, from offsets clamped into the arrays, so a wave keeps RPT x CPL weight
+// loads in flight without branches.  Clamped duplicates are harmless: a
+// chunk past the row end gets x = 0 (contributes nothing) and a row past N
+// is never stored.  Weights, scales and zeros are read with buffer loads:
+// the row offset is wave-uniform (SGPR), the lane offset 32-bit.
+template <int S, int CPL, int RPT>
+__global__ __launch_bounds__(kThreads) void gemv_int4_kernel(
+    const u32x4_t* __restrict__ qw, const uint16_t* __restrict__ s, const uint16_t* __restrict__ z,
+    const u32x4_t* __restrict__ x, uint16_t* __restrict__ y, int C, int N) {
+    constexpr int T = 4 / S;  // row teams per workgroup
+    __shared__ float part[S][T * RPT];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int slice = wave % S;
+    const int team = wave / S;
+    const int G = C >> 2;  // groups of 128 per row
+    const uint32_t row_bytes = (uint32_t)C * 16u;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(qw, (uint32_t)N * row_bytes);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, (uint32_t)N * (uint32_t)G * 2u);
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(z, (uint32_t)N * (uint32_t)G * 2u);
+
+    int c[CPL];
+    bool ok[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int ci = slice * kWave * CPL + i * kWave + lane;
+        ok[i] = ci < C;
+        c[i] = ok[i] ? ci : C - 1;
+    }
+
+    // x first (small, cache-resident): its pairs are built while the weights stream in.
+    u32x4_t xraw[CPL][4];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) xraw[i][p] = x[4 * c[i] + p];
+
+    const int row0 = (blockIdx.x * T + team) * RPT;
+    u32x4_t wv[RPT][CPL];
+    uint16_t sraw[RPT][CPL], zraw[RPT][CPL];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const uint32_t row = (uint32_t)min(row0 + r, N - 1);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            wv[r][i] = buf_load_b128<kAuxNontemporal>(rw, (uint32_t)c[i] * 16u, row * row_bytes);
+    }
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const uint32_t row = (uint32_t)min(row0 + r, N - 1);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const uint32_t goff = (uint32_t)(c[i] >> 2) * 2u;
+            sraw[r][i] = buf_load_u16(rs, goff, row * (uint32_t)G * 2u);
+            zraw[r][i] = buf_load_u16(rz, goff, row * (uint32_t)G * 2u);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load above ahead of the math below
+
+    uint32_t xp[CPL][16];
+    float sx[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        sx[i] = x_chunk_pairs(xraw[i], xp[i]);
+        if (!ok[i]) {
+            sx[i] = 0.f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) xp[i][j] = 0u;
+        }
+    }
+
+    const uint32_t bias = vgpr_const(kInt4BiasPair);
+    float acc[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        acc[r] = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const float d = chunk_dot(wv[r][i], xp[i], bias);
+            const float zb = f16_to_f32(zraw[r][i]) + 128.f;
+            acc[r] = __builtin_fmaf(f16_to_f32(sraw[r][i]), __builtin_fmaf(-zb, sx[i], d), acc[r]);
+        }
+    }
+
+    const float total = reduce_rows<RPT>(acc, lane);
+    constexpr int kLanesPerRow = kWave / RPT;
+    if ((lane % kLanesPerRow) == 0) part[slice][team * RPT + lane / kLanesPerRow] = total;
+    __syncthreads();
+    if (threadIdx.x < T * RPT) {
+        float t = 0.f;
+#pragma unroll
+        for (int k = 0; k < S; ++k) t += part[k][threadIdx.x];
+        const int row = blockIdx.x * (T * RPT) + threadIdx.x;
+        if (row < N) y[row] = f32_to_bf16(t);
+    }
+}
+
+template <int S, int CPL, int RPT>
+hipError_t launch_shape(const void* x, const int32_t* qw, const void* s, const void* z, void* y,
+                        int C, int N, hipStream_t stream) {
+    constexpr int T = 4 / S;
+    const int rows_per_block = T * RPT;
+    const unsigned blocks = (unsigned)((N + rows_per_block - 1) / rows_per_block);
+    gemv_int4_kernel<S, CPL, RPT><<<blocks, kThreads, 0, stream>>>(
+        reinterpret_cast<const u32x4_t*>(qw), static_cast<const uint16_t*>(s),
+        static_cast<const uint16_t*>(z), static_cast<const u32x4_t*>(x),
+        static_cast<uint16_t*>(y), C, N);
+    return hipGetLastError();
+}
+
+template <int S, int CPL>
+hipError_t launch_rpt(const void* x, const int32_t* qw, const void* s, const void* z, void* y,
+                      int C, int N, hipStream_t stream) {
+    constexpr int T = 4 / S;
+    auto blocks = [&](int rpt) { return (N + T * rpt - 1) / (T * rpt); };
+    if (blocks(8) >= W4_GEMV_MIN_BLOCKS) return launch_shape<S, CPL, 8>(x, qw, s, z, y, C, N, stream);
+    if (blocks(4) >= W4_GEMV_MIN_BLOCKS) return launch_shape<S, CPL, 4>(x, qw, s, z, y, C, N, stream);
+    if (blocks(2) >= W4_GEMV_MIN_BLOCKS) return launch_shape<S, CPL, 2>(x, qw, s, z, y, C, N, stream);
+    return launch_shape<S, CPL, 1>(x, qw, s, z, y, C, N, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_int4(const void* x, const int32_t* qw, const void* s, const void* z,
+                            void* y, int K, int N, hipStream_t stream) {
+    const int C = K / 32;
+    const RowSplit rs = row_split(C);
+    switch (rs.slices * 16 + rs.cpl) {
+        case 1 * 16 + 1: return launch_rpt<1, 1>(x, qw, s, z, y, C, N, stream);
+        case 1 * 16 + 2: return launch_rpt<1, 2>(x, qw, s, z, y, C, N, stream);
+        case 2 * 16 + 2: return launch_rpt<2, 2>(x, qw, s, z, y, C, N, stream);
+        case 4 * 16 + 2: return launch_rpt<4, 2>(x, qw, s, z, y, C, N, stream);
+        case 4 * 16 + 3: return launch_rpt<4, 3>(x, qw, s, z, y, C, N, stream);
+        case 4 * 16 + 4: return launch_rpt<4, 4>(x, qw, s, z, y, C, N, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace w4

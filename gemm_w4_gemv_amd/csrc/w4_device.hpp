@@ -1,0 +1,169 @@
+// Device helpers shared by the gfx950 kernels: bit formats, nibble unpacking
+// and the few CDNA4 instructions the kernels are built around.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4 {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------ buffer loads
+// Raw buffer loads: an SGPR resource (base, size) plus a 32-bit per-lane byte
+// offset and a wave-uniform SGPR byte offset.  This keeps 64-bit address
+// arithmetic off the VALU, and a lane offset at or past ``bytes`` reads 0
+// instead of faulting.  Word 3 of the descriptor is the raw 32-bit data
+// format of the gfx9 family.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kAuxNontemporal = 2;  // stream past the caches: read once
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
+template <int kAux = 0>
+__device__ __forceinline__ u32x4_t buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kAux));
+}
+
+__device__ __forceinline__ uint16_t buf_load_u16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+}
+
+// ------------------------------------------------------------------ formats
+__device__ __forceinline__ float f16_to_f32(uint16_t bits) {
+    return (float)__builtin_bit_cast(_Float16, bits);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __builtin_bit_cast(float, bits16 << 16);
+}
+
+// float -> bfloat16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2_t v;
+    v.x = (__bf16)lo;
+    v.y = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// c + a.lo * b.lo + a.hi * b.hi with bf16 pairs and an FP32 accumulator (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ------------------------------------------------------------------- INT4
+// Packed INT4: bits 4j..4j+3 of a word hold the code of k = 8p + j.
+
+// Biased bfloat16 pairs for the GEMV's dot2 path.  bf16 0x4300 is 128.0 and
+// its unit in the last place is 1, so 0x4300 | q is exactly 128 + q.  Pair j
+// (j = 0..3) holds (128 + q_j, 128 + q_{j+4}): nibbles j and j+4 sit 16 bits
+// apart, so one mask extracts both.
+//
+// ``bias`` must be 0x43004300 held in a VGPR (see vgpr_const): gfx9 VOP3
+// instructions take no literal operand, and with the mask in an SGPR and the
+// bias in a VGPR each pair is one v_bitop3_b32 / v_and_or_b32 after the shift.
+__device__ __forceinline__ void int4_word_biased_pairs(uint32_t w, uint32_t bias, uint32_t out[4]) {
+    constexpr uint32_t kMask = 0x000F000Fu;
+    out[0] = (w & kMask) | bias;
+    out[1] = ((w >> 4) & kMask) | bias;
+    out[2] = ((w >> 8) & kMask) | bias;
+    out[3] = ((w >> 12) & kMask) | bias;
+}
+
+constexpr uint32_t kInt4BiasPair = 0x43004300u;  // bf16 pair (128.0, 128.0)
+
+// A constant the compiler must keep in a VGPR and cannot fold into literals.
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// x pairs matching int4_word_biased_pairs: from the eight bf16 x[8p .. 8p+7]
+// held as four words (x0,x1), (x2,x3), (x4,x5), (x6,x7), build
+// (x_j, x_{j+4}) for j = 0..3.
+__device__ __forceinline__ void x_pairs_for_biased(const uint32_t xw[4], uint32_t out[4]) {
+    out[0] = (xw[0] & 0xFFFFu) | (xw[2] << 16);
+    out[1] = (xw[0] >> 16) | (xw[2] & 0xFFFF0000u);
+    out[2] = (xw[1] & 0xFFFFu) | (xw[3] << 16);
+    out[3] = (xw[1] >> 16) | (xw[3] & 0xFFFF0000u);
+}
+
+// Exact FP32 dequantisation of one word: out[j] = (q_j - z) * s.  (q - z) has
+// at most 5 significant bits and s 11, so the product is exact in FP32.
+__device__ __forceinline__ void int4_word_dequant_f32(uint32_t w, float s, float z, float out[8]) {
+    const uint32_t lo = w & 0x0F0F0F0Fu;         // codes of k = 8p + 0, 2, 4, 6 in bytes 0..3
+    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes of k = 8p + 1, 3, 5, 7
+    // (float)((v >> 8i) & 0xFF) is a single v_cvt_f32_ubyte{i}.
+    out[0] = ((float)(lo & 0xFFu) - z) * s;
+    out[1] = ((float)(hi & 0xFFu) - z) * s;
+    out[2] = ((float)((lo >> 8) & 0xFFu) - z) * s;
+    out[3] = ((float)((hi >> 8) & 0xFFu) - z) * s;
+    out[4] = ((float)((lo >> 16) & 0xFFu) - z) * s;
+    out[5] = ((float)((hi >> 16) & 0xFFu) - z) * s;
+    out[6] = ((float)(lo >> 24) - z) * s;
+    out[7] = ((float)(hi >> 24) - z) * s;
+}
+
+// ------------------------------------------------------------------- FP4
+// One byte holds two E2M1 codes: low nibble = even k, high nibble = odd k.
+// v_cvt_scalef32_pk_bf16_fp4 converts the two codes of byte ``sel`` to a bf16
+// pair (even k in the low half).  With a scale of 1.0 the result is the exact
+// E2M1 value; the real BF16 scale is applied afterwards in FP32.
+template <int kSel>
+__device__ __forceinline__ uint32_t fp4_byte_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, kSel));
+}
+
+__device__ __forceinline__ void fp4_word_pairs(uint32_t w, uint32_t out[4]) {
+    out[0] = fp4_byte_to_bf16x2<0>(w);
+    out[1] = fp4_byte_to_bf16x2<1>(w);
+    out[2] = fp4_byte_to_bf16x2<2>(w);
+    out[3] = fp4_byte_to_bf16x2<3>(w);
+}
+
+// -------------------------------------------------------------- reductions
+// Reduce R per-lane values (one per row) across the 64 lanes of a wave.
+// Each step halves the rows a lane carries by exchanging the other half with
+// the partner lane, so R rows cost R - 1 + log2(64 / R) exchanges instead of
+// 6 R.  On return every lane holds the total of row lane / (64 / R).
+template <int R, int kOff>
+struct RowReduce {
+    static __device__ __forceinline__ void run(float* v, int lane) {
+        if constexpr (R > 1) {
+            constexpr int H = R / 2;
+            const bool upper = (lane & kOff) != 0;
+#pragma unroll
+            for (int i = 0; i < H; ++i) {
+                const float send = upper ? v[i] : v[i + H];
+                const float keep = upper ? v[i + H] : v[i];
+                v[i] = keep + __shfl_xor(send, kOff, kWave);
+            }
+            RowReduce<H, kOff / 2>::run(v, lane);
+        } else if constexpr (kOff >= 1) {
+            v[0] += __shfl_xor(v[0], kOff, kWave);
+            RowReduce<1, kOff / 2>::run(v, lane);
+        }
+    }
+};
+
+template <int R>
+__device__ __forceinline__ float reduce_rows(float (&v)[R], int lane) {
+    static_assert(R >= 1 && R <= 64 && (R & (R - 1)) == 0, "R must be a power of two");
+    RowReduce<R, 32>::run(v, lane);
+    return v[0];
+}
+
+}  // namespace w4

@@ -1,0 +1,42 @@
+// Launchers behind the C ABI.  Arguments are already validated by the caller
+// (w4_api.hip); each launcher only picks a launch shape and enqueues kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4 {
+
+hipError_t launch_gemv_int4(const void* x, const int32_t* qw, const void* s, const void* z,
+                            void* y, int K, int N, hipStream_t stream);
+
+size_t gemm_int4_workspace_bytes(int M, int K, int N);
+hipError_t launch_gemm_int4(const void* x, const int32_t* qw, const void* s, const void* z,
+                            void* y, int M, int K, int N, void* workspace, hipStream_t stream);
+
+hipError_t launch_moe_gemv_fp4(const void* x, int64_t x_stride, const uint8_t* qw,
+                               const void* s, const int32_t* ids, void* y, int E,
+                               int num_experts, int K, int N, hipStream_t stream);
+
+hipError_t launch_dequant_int4(const int32_t* qw, const void* s, const void* z, float* out_f32,
+                               void* out_bf16, int K, int N, hipStream_t stream);
+hipError_t launch_dequant_fp4(const uint8_t* qw, const void* s, float* out_f32, void* out_bf16,
+                              int K, int N, hipStream_t stream);
+
+// Split of the K range of a GEMV row over the four waves of a workgroup.
+// A row has C = K / 32 chunks of 16 bytes.  Each lane owns up to ``cpl``
+// chunks of one K-slice and keeps their x values in registers; ``slices``
+// waves share a row when the row is too long for one wave.
+struct RowSplit {
+    int slices;  // 1, 2 or 4 waves per row
+    int cpl;     // chunks per lane, 1..4
+};
+
+inline RowSplit row_split(int chunks) {
+    if (chunks <= 128) return {1, (chunks + 63) / 64};
+    if (chunks <= 256) return {2, 2};
+    return {4, (chunks + 255) / 256};
+}
+
+}  // namespace w4

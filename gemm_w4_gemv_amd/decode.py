@@ -1,0 +1,58 @@
+"""The decode step's GEMV chain captured once into a HIP graph.
+
+"Lab 5: Gemma4 端到端推理优化", section "CUDA Graph": after the fused GEMV the
+remaining cost was launch and Python overhead, so the whole decode step is
+captured once into a static graph and replayed once per token; the graph
+needs static buffers.  Here the step is the chain of INT4 linears of every
+layer in launch order (q, k, v, o, gate, up, down), each an ``w4_gemv``
+recorded on one stream; every linear keeps its own static input and output
+buffers, so one replay recomputes every output.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import w4_gemv, w4_graph_begin, w4_graph_end, W4Graph
+
+
+class DecodeStep:
+    """A captured chain of ``w4_gemv`` calls.
+
+    ``linears`` is a sequence of dicts with device tensors ``qw`` (int32
+    [N, K/8]), ``s``, ``z`` (float16 [N, K/128]), ``x`` (bfloat16 [K]) and
+    ``y`` (bfloat16 [N]).  The tensors must stay alive while the graph does.
+    """
+
+    def __init__(self, linears, stream: torch.cuda.Stream | None = None):
+        self.linears = list(linears)
+        self.stream = stream if stream is not None else torch.cuda.Stream()
+        self.graph: W4Graph | None = None
+
+    def run_eager(self) -> None:
+        """Launch the chain directly on the step's stream (no graph)."""
+        for lin in self.linears:
+            w4_gemv(lin["x"], lin["qw"], lin["s"], lin["z"], lin["y"], stream=self.stream)
+
+    def capture(self) -> W4Graph:
+        """Record the chain into a graph (nothing runs during capture)."""
+        if self.graph is not None:
+            self.graph.destroy()
+        torch.cuda.synchronize()
+        w4_graph_begin(self.stream)
+        try:
+            self.run_eager()
+        finally:
+            # ending the capture also ends it after a failed launch
+            graph = w4_graph_end(self.stream)
+        self.graph = graph
+        return graph
+
+    def replay(self) -> None:
+        if self.graph is None:
+            self.capture()
+        self.graph.replay(self.stream)
+
+    def destroy(self) -> None:
+        if self.graph is not None:
+            self.graph.destroy()
+            self.graph = None

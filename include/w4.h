@@ -1,0 +1,187 @@
+/*
+ * w4.h -- C ABI of the fused 4-bit-weight x BF16 GEMV / GEMM library (MI355X, gfx950).
+ *
+ * The operation.  A linear layer y = x * W^T (``F.linear`` semantics, no bias)
+ * whose weight W[N][K] is stored packed in 4 bits and is never expanded to
+ * BF16 in device memory:
+ *
+ *   INT4 (GPTQ-style, asymmetric): W[n][k] = (q[n][k] - z[n][k/128]) * s[n][k/128]
+ *     -- "Lab 5: Gemma4 端到端推理优化", sections "量化正确性" (GPTQ INT4,
+ *        group 128, asymmetric), "最终配置" (FP16 scale) and "INT4 融合 GEMV"
+ *        (fused GEMV: packed INT4 read once, unpacked in registers, per-group
+ *        scale/zero applied, dot with the BF16 input; M = 1 decode and an
+ *        M = 128 prefill path).
+ *   FP4 (E2M1):  W[n][k] = e2m1(c[n][k]) * s[n][k/32]
+ *     -- "DeepSeek V4 Triton FP4 优化实战", section "深度分析" item 2 (even k
+ *        in the low nibble, odd k in the high nibble) and item 4 (6 active
+ *        experts x 2 FC per layer, each at M = 1).
+ *
+ * Arithmetic: products and sums in FP32; the output is rounded once to BF16,
+ * round-to-nearest-even.  Summation order is unspecified but fixed: the same
+ * call on the same inputs returns the same bits (no floating-point atomics).
+ *
+ * Layouts (all row-major, contiguous, little-endian):
+ *   x       bf16   [M][K]                activations (M = 1 for the GEMVs)
+ *   qw      int32  [N][K/8]              INT4 codes; bits 4j..4j+3 of word p hold k = 8p + j
+ *   s, z    fp16   [N][K/128]            INT4 scale and zero point (zero integer-valued, 0..15)
+ *   qw_fp4  uint8  [experts][N][K/2]     E2M1 codes; low nibble = even k, high nibble = odd k
+ *   s_fp4   bf16   [experts][N][K/32]    FP4 scale (a full BF16 multiplier)
+ *   y       bf16   [M][N]                output
+ * BF16 and FP16 buffers are passed as pointers to their 16-bit patterns.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers named as device pointers must point to device memory of the
+ *     current HIP device.  The caller owns every buffer, including the GEMM
+ *     workspace; the library never allocates, frees or reads device memory
+ *     on the host and never synchronises, so every call can be captured into
+ *     a HIP graph.
+ *   - ``stream`` is a hipStream_t (NULL = the default stream).  Calls are
+ *     asynchronous: a return of W4_OK means the work was enqueued.
+ *   - Arguments are validated on the host before any HIP call.  On a
+ *     validation error nothing is launched and an error status is returned;
+ *     w4_last_error() then describes it.
+ *   - M = 0 or N = 0 (or E = 0) is an empty problem: W4_OK, nothing launched.
+ *   - Outputs must not overlap any input (checked from the address ranges).
+ *   - Not checked (would need a device read): zero points integer-valued in
+ *     0..15 and finite inputs.  Expert ids outside [0, num_experts) are
+ *     checked on the device: that slot's outputs are set to NaN and no
+ *     weight is read for it.
+ */
+#ifndef W4_H
+#define W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define W4_API __attribute__((visibility("default")))
+#else
+#define W4_API
+#endif
+
+typedef enum w4_status {
+    W4_OK = 0,
+    W4_ERR_NULL = 1,        /* a required pointer is NULL */
+    W4_ERR_SHAPE = 2,       /* negative size; K not a positive multiple of the group; K above the limit */
+    W4_ERR_UNSUPPORTED = 3, /* group size other than 128 (INT4) */
+    W4_ERR_ALIGN = 4,       /* a pointer is not aligned as its entry point requires */
+    W4_ERR_WORKSPACE = 5,   /* GEMM workspace NULL or smaller than w4_gemm_workspace_bytes() */
+    W4_ERR_ALIAS = 6,       /* an output range overlaps an input range */
+    W4_ERR_ARG = 7,         /* other invalid argument (stride, expert count, NULL graph or stream) */
+    W4_ERR_HIP = 8          /* the HIP runtime reported an error (see w4_last_error()) */
+} w4_status;
+
+/* Largest K accepted by w4_gemv / w4_moe_gemv (registers hold the whole x row slice). */
+#define W4_GEMV_MAX_K 32768
+/* Largest packed weight matrix (N * K / 2 bytes, per expert for FP4) of one
+ * w4_gemv / w4_moe_gemv call: the kernels address it with 32-bit offsets. */
+#define W4_GEMV_MAX_MATRIX_BYTES 4294967295ull
+#define W4_INT4_GROUP 128
+#define W4_FP4_GROUP 32
+
+/* ABI version of this header (bumped on any incompatible change). */
+W4_API int w4_abi_version(void);
+
+/* Name of a status code (static string, never NULL). */
+W4_API const char* w4_status_string(w4_status status);
+
+/* Description of the most recent error returned on the calling thread (static per thread). */
+W4_API const char* w4_last_error(void);
+
+/*
+ * w4_gemv -- decode GEMV, M = 1, INT4 weights.
+ *   y[n] = bf16( sum_k (q[n][k] - z[n][k/g]) * s[n][k/g] * x[k] ),  n < N
+ * "Lab 5: Gemma4 端到端推理优化", section "INT4 融合 GEMV": weights read once,
+ * unpacked in registers, the input vector reused from registers or LDS.
+ *   x   device bf16 [K], 16-byte aligned      qw  device int32 [N][K/8], 16-byte aligned
+ *   s,z device fp16 [N][K/g], 2-byte aligned  y   device bf16 [N], 2-byte aligned
+ *   K   multiple of g, 0 < K <= W4_GEMV_MAX_K;  N >= 0;  g must be 128;
+ *       N * K / 2 <= W4_GEMV_MAX_MATRIX_BYTES.
+ * Errors: W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_UNSUPPORTED, W4_ERR_ALIGN, W4_ERR_ALIAS, W4_ERR_HIP.
+ */
+W4_API w4_status w4_gemv(const void* x, const int32_t* qw, const void* s, const void* z,
+                         void* y, int K, int N, int g, void* stream);
+
+/*
+ * w4_gemm -- prefill GEMM, any M >= 0 (built for M = 128), INT4 weights.
+ *   y[m][n] = bf16( sum_k bf16((q[n][k] - z[n][k/g]) * s[n][k/g]) * x[m][k] )
+ * "Lab 5: Gemma4 端到端推理优化", sections "Triton 反量化 + cuBLAS" (prefill:
+ * dequantised BF16 weights into a tensor-core GEMM) and "INT4 融合 GEMV"
+ * (equivalence tested at M = 128).  Here the weight tile is dequantised into
+ * LDS (BF16, round-to-nearest-even, the matrix-core operand) and never
+ * written to device memory.
+ *   x   device bf16 [M][K], 16-byte aligned   qw, s, z as for w4_gemv
+ *   y   device bf16 [M][N], 2-byte aligned
+ *   workspace  device memory of at least w4_gemm_workspace_bytes(M, K, N, g)
+ *              bytes, 16-byte aligned (may be NULL when that size is 0).  It
+ *              holds FP32 split-K partial sums; its contents on entry are
+ *              ignored and on return are unspecified.  Calls that share one
+ *              workspace must be ordered (same stream).
+ * Errors: as w4_gemv, plus W4_ERR_WORKSPACE.
+ */
+W4_API size_t w4_gemm_workspace_bytes(int M, int K, int N, int g);
+W4_API w4_status w4_gemm(const void* x, const int32_t* qw, const void* s, const void* z,
+                         void* y, int M, int K, int N, int g,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * w4_moe_gemv -- FP4 expert GEMVs, M = 1 per slot.
+ *   y[e][n] = bf16( sum_k e2m1(c[ids[e]][n][k]) * s[ids[e]][n][k/32] * x_e[k] ),  e < E
+ *   with x_e = x + e * x_stride (elements); x_stride = 0 shares one vector.
+ * "DeepSeek V4 Triton FP4 优化实战", "深度分析" items 2 and 4.
+ *   x          device bf16, 16-byte aligned; x_stride >= 0, a multiple of 8
+ *   qw_fp4     device uint8 [num_experts][N][K/2], 16-byte aligned
+ *   s_fp4      device bf16 [num_experts][N][K/32], 2-byte aligned
+ *   expert_ids device int32 [E], 4-byte aligned (read on the device)
+ *   y          device bf16 [E][N], 2-byte aligned
+ *   K multiple of 32, 0 < K <= W4_GEMV_MAX_K;  E >= 0;  num_experts >= 1;
+ *   N * K / 2 <= W4_GEMV_MAX_MATRIX_BYTES.
+ * Errors: W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_ALIAS, W4_ERR_ARG, W4_ERR_HIP.
+ */
+W4_API w4_status w4_moe_gemv(const void* x, int64_t x_stride, const uint8_t* qw_fp4,
+                             const void* s_fp4, const int32_t* expert_ids, void* y,
+                             int E, int num_experts, int K, int N, void* stream);
+
+/*
+ * Decode-step graphs.  "Lab 5: Gemma4 端到端推理优化", section "CUDA Graph":
+ * the whole decode step is captured once and replayed once per token, which
+ * needs static buffers.  w4_graph_begin starts capturing ``stream`` (which
+ * must not be NULL); every library call made on that stream by this thread
+ * until w4_graph_end is recorded instead of run; w4_graph_end ends the
+ * capture and instantiates the graph.  w4_graph_replay enqueues one replay on
+ * ``stream``.  The graph keeps the pointers it was captured with: those
+ * buffers must stay allocated until w4_graph_destroy.  A failed w4_graph_end
+ * leaves *graph NULL.
+ * Errors: W4_ERR_ARG (NULL stream or graph), W4_ERR_HIP.
+ */
+typedef struct w4_graph* w4_graph_t;
+W4_API w4_status w4_graph_begin(void* stream);
+W4_API w4_status w4_graph_end(void* stream, w4_graph_t* graph);
+W4_API w4_status w4_graph_replay(w4_graph_t graph, void* stream);
+W4_API void w4_graph_destroy(w4_graph_t graph);
+
+/*
+ * Test-only dequantisers, sharing the device unpack code of the GEMM and the
+ * FP4 GEMV.  They write the FP32 value of every weight (exact: at most 15
+ * significant bits) and/or its BF16 round-to-nearest-even, so the packed
+ * formats can be compared bit for bit with an independent reference.
+ *   w4_dequant_int4: qw, s, z as for w4_gemv; out_f32 float [N][K];
+ *                    out_bf16 bf16 [N][K]; either output may be NULL, not both.
+ *   w4_dequant_fp4:  qw_fp4 uint8 [N][K/2], s_fp4 bf16 [N][K/32] (one expert).
+ * Errors: as w4_gemv.
+ */
+W4_API w4_status w4_dequant_int4(const int32_t* qw, const void* s, const void* z,
+                                 float* out_f32, void* out_bf16, int K, int N, int g,
+                                 void* stream);
+W4_API w4_status w4_dequant_fp4(const uint8_t* qw_fp4, const void* s_fp4, float* out_f32,
+                                void* out_bf16, int K, int N, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4_H */

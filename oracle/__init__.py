@@ -123,7 +123,7 @@ def fp4_codes(qw) -> np.ndarray:
 
 def dequant_fp4(qw, s_bits, group: int = FP4_GROUP) -> np.ndarray:
     """``W[..., n, k] = e2m1(code[..., n, k]) * s[..., n, k // 32]`` in float64 (reading 4)."""
-    v = e2m1_value(fp4_codes(qw))
+    v = e2m1_value(np.arange(16))[fp4_codes(qw)]  # the formula evaluated once per code
     s = np.repeat(bf16_to_f64(s_bits), group, axis=-1)
     assert s.shape == v.shape, "scale shape does not match K/32"
     return v * s

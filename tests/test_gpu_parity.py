@@ -1,0 +1,322 @@
+"""GPU parity of every entry point against the FP64 oracle, through the C ABI.
+
+Small shapes are compared in full; the full-size workloads (3840 x 3840
+GEMV, the 336-linear decode step captured in a graph exactly as the bench
+times it, the M = 128 prefill shapes, the 262144-row logits GEMV and the
+six-expert FP4 MoE pair) are compared in full where the oracle is quick and
+on sampled rows otherwise.  Dequantised tiles must match bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+from parity import check_outputs
+
+pytestmark = pytest.mark.gpu
+
+w4 = pytest.importorskip("gemm_w4_gemv_amd")
+from gemm_w4_gemv_amd import host  # noqa: E402
+from gemm_w4_gemv_amd.decode import DecodeStep  # noqa: E402
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def run_gemv(lin_np, x_bits):
+    t = host.int4_tensors(lin_np)
+    x = host.bf16_tensor(x_bits)
+    y = torch.empty(t["qw"].shape[0], dtype=torch.bfloat16, device=DEV)
+    w4.w4_gemv(x, t["qw"], t["s"], t["z"], y)
+    torch.cuda.synchronize()
+    return host.bf16_values(y)
+
+
+def int4_ref(lin_np, x_bits, rows=None):
+    """Oracle output and the per-row max |W| of the selected rows."""
+    qw, s, z = lin_np["qw"], lin_np["s"], lin_np["z"]
+    if rows is not None:
+        qw, s, z = qw[rows], s[rows], z[rows]
+    W = oracle.dequant_int4(qw, s, z)
+    y = oracle.linear(oracle.bf16_to_f64(np.atleast_2d(x_bits)), W)
+    return y, np.abs(W).max(axis=1)
+
+
+def xnorm(x_bits):
+    return np.linalg.norm(oracle.bf16_to_f64(np.atleast_2d(x_bits)), axis=1)
+
+
+# ------------------------------------------------------------ dequant tiles
+@pytest.mark.parametrize("N,K", [(37, 256), (64, 3840), (3, 15360), (130, 4096), (1, 128)])
+def test_dequant_int4_bit_exact(N, K):
+    lin = si.int4_linear(11, (N, K), K, N)
+    t = host.int4_tensors(lin)
+    f32 = torch.empty(N, K, dtype=torch.float32, device=DEV)
+    b16 = torch.empty(N, K, dtype=torch.bfloat16, device=DEV)
+    w4.w4_dequant_int4(t["qw"], t["s"], t["z"], f32, b16)
+    torch.cuda.synchronize()
+    W = oracle.dequant_int4(lin["qw"], lin["s"], lin["z"])
+    got = f32.cpu().numpy()
+    assert np.array_equal(got.astype(np.float64), W)
+    assert np.array_equal(got.view(np.uint32), W.astype(np.float32).view(np.uint32))  # same zero signs too
+    assert np.array_equal(host.bits_of(b16), oracle.bf16_bits(W))
+
+
+@pytest.mark.parametrize("N,K", [(33, 64), (128, 4096), (7, 2048), (2, 32)])
+def test_dequant_fp4_bit_exact(N, K):
+    pool = si.fp4_pool(12, (N, K), 1, K, N)
+    qw = torch.from_numpy(pool["qw"][0]).to(DEV)
+    s = host.bf16_tensor(pool["s"][0])
+    f32 = torch.empty(N, K, dtype=torch.float32, device=DEV)
+    b16 = torch.empty(N, K, dtype=torch.bfloat16, device=DEV)
+    w4.w4_dequant_fp4(qw, s, f32, b16)
+    torch.cuda.synchronize()
+    W = oracle.dequant_fp4(pool["qw"][0], pool["s"][0])
+    got = f32.cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, W)  # +0 == -0: the sign of a zero code cannot change a sum
+    bits, ref = host.bits_of(b16), oracle.bf16_bits(W)
+    nz = W != 0
+    assert np.array_equal(bits[nz], ref[nz])
+    assert np.all((bits[~nz] & 0x7FFF) == 0)
+
+
+# --------------------------------------------------------------- INT4 GEMV
+GEMV_SHAPES = [
+    (128, 1), (128, 7), (256, 33), (384, 5),      # one group .. a few, tiny N
+    (3840, 3840),                                 # the single-GEMV workload
+    (4096, 130), (3840, 2051),                    # q/o row length, ragged N
+    (8192, 64), (8320, 17),                       # two waves per row, and a ragged slice
+    (15360, 67),                                  # four waves per row (down projection)
+    (20480, 40), (32768, 9),                      # three and four chunks per lane (K limit)
+]
+
+
+@pytest.mark.parametrize("K,N", GEMV_SHAPES)
+def test_gemv_parity(K, N):
+    print(f"gemv K={K} N={N}", flush=True)
+    lin, x = si.single_gemv(K, N, seed=3)
+    y = run_gemv(lin, x)
+    y_ref, wmax = int4_ref(lin, x)
+    check_outputs(y, y_ref[0], xnorm(x), wmax, f"gemv K={K} N={N}")
+
+
+def test_gemv_single_workload_seed0():
+    """The 3840 x 3840 single GEMV with its own seed-0 inputs, every output."""
+    lin, x = si.single_gemv()
+    y = run_gemv(lin, x)
+    y_ref, wmax = int4_ref(lin, x)
+    check_outputs(y, y_ref[0], xnorm(x), wmax, "single gemv")
+
+
+def test_gemv_logits_sampled():
+    """K3840 -> N262144 at full size; oracle on 3000 sampled rows plus both ends."""
+    lin, x = si.logits()
+    y = run_gemv(lin, x)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(262144 - 8, 262144),
+                                     si.rng(5, 1).choice(262144, 3000, replace=False)]))
+    y_ref, wmax = int4_ref(lin, x, rows)
+    check_outputs(y[rows], y_ref[0], xnorm(x), wmax, "logits")
+
+
+def test_gemv_deterministic_and_guarded():
+    """Two calls give identical bits; memory around the output is untouched."""
+    lin, x_bits = si.single_gemv(3840, 1000, seed=4)
+    t = host.int4_tensors(lin)
+    x = host.bf16_tensor(x_bits)
+    pad = 64
+    buf = torch.full((1000 + 2 * pad,), 7.0, dtype=torch.bfloat16, device=DEV)
+    y = buf[pad:pad + 1000]
+    w4.w4_gemv(x, t["qw"], t["s"], t["z"], y)
+    first = y.clone()
+    w4.w4_gemv(x, t["qw"], t["s"], t["z"], y)
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), y.view(torch.int16))
+    assert torch.all(buf[:pad] == 7.0) and torch.all(buf[pad + 1000:] == 7.0)
+
+
+def test_gemv_empty_is_noop():
+    """N = 0 returns W4_OK and launches nothing (the output buffer keeps its contents)."""
+    t = host.int4_tensors(si.int4_linear(1, (0,), 256, 4))
+    x = host.bf16_tensor(si.bf16_normal(1, (0,), (256,)))
+    y = torch.full((8,), 1.0, dtype=torch.bfloat16, device=DEV)
+    assert w4.lib.w4_gemv(x.data_ptr(), t["qw"].data_ptr(), t["s"].data_ptr(), t["z"].data_ptr(),
+                          y.data_ptr(), 256, 0, 128, None) == 0
+    torch.cuda.synchronize()
+    assert torch.all(y == 1.0)
+
+
+# ---------------------------------------------------------- decode-step graph
+def test_decode_step_graph_full_size():
+    """All 336 linears of the decode step, captured and replayed as the bench times them.
+
+    Graph replays equal the eager chain bit for bit (replays interleaved with
+    other work), and every one of the 336 outputs matches the oracle on
+    sampled rows.
+    """
+    specs = si.decode_step_specs()
+    lins, host_in = [], []
+    for layer, idx, name, K, N in specs:
+        lin_np, x_bits = si.decode_linear(layer, idx)
+        t = host.int4_tensors(lin_np)
+        t["x"] = host.bf16_tensor(x_bits)
+        t["y"] = torch.zeros(N, dtype=torch.bfloat16, device=DEV)
+        lins.append(t)
+        host_in.append((lin_np, x_bits))
+    step = DecodeStep(lins)
+    torch.cuda.synchronize()  # the zero fills above ran on the default stream
+    step.run_eager()
+    torch.cuda.synchronize()
+    eager = [t["y"].clone() for t in lins]
+    for t in lins:
+        t["y"].zero_()
+    step.capture()
+    for rep in range(3):
+        step.replay()
+        step.stream.synchronize()
+        for t, e in zip(lins, eager):
+            assert torch.equal(t["y"].view(torch.int16), e.view(torch.int16)), f"replay {rep} differs"
+        for t in lins:  # eager work between replays
+            t["y"].fill_(3.0)
+        torch.cuda.synchronize()
+    step.replay()
+    step.stream.synchronize()
+    g = si.rng(6, 0)
+    for (layer, idx, name, K, N), (lin_np, x_bits), t in zip(specs, host_in, lins):
+        rows = np.unique(np.concatenate([[0, N - 1], g.choice(N, 24, replace=False)]))
+        y = host.bf16_values(t["y"])[rows]
+        y_ref, wmax = int4_ref(lin_np, x_bits, rows)
+        check_outputs(y, y_ref[0], xnorm(x_bits), wmax, f"layer {layer} {name}")
+    step.destroy()
+
+
+# ------------------------------------------------------------- prefill GEMM
+def run_gemm(lin_np, x_bits):
+    t = host.int4_tensors(lin_np)
+    x = host.bf16_tensor(x_bits)
+    M, K = x.shape
+    N = t["qw"].shape[0]
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    nbytes = w4.w4_gemm_workspace_bytes(M, K, N)
+    ws = torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=DEV) if nbytes else None
+    w4.w4_gemm(x, t["qw"], t["s"], t["z"], y, workspace=ws)
+    torch.cuda.synchronize()
+    return host.bf16_values(y), (nbytes > 0)
+
+
+@pytest.mark.parametrize("shape_index", [0, 1])
+def test_gemm_prefill_full(shape_index):
+    """M = 128 prefill at both full shapes, every output (the K15360 shape splits K)."""
+    lin, x = si.prefill(shape_index)
+    y, split = run_gemm(lin, x)
+    assert split == (shape_index == 1)
+    y_ref, wmax = int4_ref(lin, x)
+    check_outputs(y, y_ref, xnorm(x), wmax, f"prefill {si.PREFILL_SHAPES[shape_index]}")
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (1, 128, 64), (5, 384, 100), (128, 256, 64), (200, 256, 130), (129, 640, 63),
+    (128, 1024, 16),     # one tile: K split eight ways
+    (64, 15360, 192),    # split K with a ragged N
+    (16, 4096, 3840),
+])
+def test_gemm_parity(M, K, N):
+    print(f"gemm M={M} K={K} N={N}", flush=True)
+    lin = si.int4_linear(21, (M, K, N), K, N)
+    x = si.bf16_normal(21, (M, K, N, 7), (M, K))
+    y, _ = run_gemm(lin, x)
+    y_ref, wmax = int4_ref(lin, x)
+    check_outputs(y, y_ref, xnorm(x), wmax, f"gemm M={M} K={K} N={N}")
+
+
+def test_gemm_deterministic():
+    lin, x_bits = si.prefill(1, M=32)
+    a, _ = run_gemm(lin, x_bits)
+    b, _ = run_gemm(lin, x_bits)
+    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+
+
+# ------------------------------------------------------------------- FP4 MoE
+@pytest.fixture(scope="module")
+def moe():
+    pools = si.moe_pools()
+    dev = [host.fp4_tensors(p) for p in pools]
+    return pools, dev
+
+
+def moe_run(dev_pool, x_bits, ids, shared):
+    x = host.bf16_tensor(x_bits)
+    idt = torch.from_numpy(np.asarray(ids, dtype=np.int32)).to(DEV)
+    N = dev_pool["qw"].shape[1]
+    y = torch.empty(len(ids), N, dtype=torch.bfloat16, device=DEV)
+    w4.w4_moe_gemv(x, dev_pool["qw"], dev_pool["s"], idt, y)
+    return y
+
+
+def test_moe_full_workload(moe):
+    """Six experts x 2 FC at full size: 120 tokens' id sets plus hand-picked ones, every output.
+
+    The oracle output of every (x, expert) pair is computed once; each id set
+    is then checked against the rows of its experts (layer-by-layer numeric
+    comparison over many expert combinations, as the DeepSeek V4 FP4 page
+    recommends in "实践启示" item 2).
+    """
+    pools, dev = moe
+    ids0, x1, x2 = si.moe_inputs(0)
+    refs = []
+    for fc, (K, N) in enumerate(si.MOE_FC):
+        xs = oracle.bf16_to_f64(np.atleast_2d(x1 if fc == 0 else x2))
+        y_all = np.empty((si.MOE_POOL, xs.shape[0], N))
+        wmax = np.empty((si.MOE_POOL, N))
+        for e in range(si.MOE_POOL):
+            W = oracle.dequant_fp4(pools[fc]["qw"][e], pools[fc]["s"][e])
+            y_all[e] = oracle.linear(xs, W)
+            wmax[e] = np.abs(W).max(axis=1)
+        refs.append((y_all, wmax, np.linalg.norm(xs, axis=1)))
+    id_sets = [si.moe_inputs(t)[0] for t in range(120)]
+    id_sets += [np.array([0, 63, 1, 62, 31, 32]), np.array([5, 5, 5, 9, 9, 0]), np.array([63] * 6)]
+    for ids in id_sets:
+        for fc in range(2):
+            y_all, wmax, xn = refs[fc]
+            y = host.bf16_values(moe_run(dev[fc], x1 if fc == 0 else x2, ids, fc == 0))
+            torch.cuda.synchronize()
+            for e, eid in enumerate(ids):
+                xi = 0 if fc == 0 else e
+                check_outputs(y[e], y_all[eid, xi], xn[xi], wmax[eid], f"fc{fc + 1} slot {e} expert {eid}")
+
+
+def test_moe_invalid_id_gives_nan_and_others_unaffected(moe):
+    pools, dev = moe
+    _, x1, _ = si.moe_inputs(1)
+    ok = host.bf16_values(moe_run(dev[0], x1, [3, 4, 5], True))
+    bad = host.bf16_values(moe_run(dev[0], x1, [3, 64, -1], True))
+    torch.cuda.synchronize()
+    assert np.array_equal(ok[0], bad[0])
+    assert np.all(np.isnan(bad[1])) and np.all(np.isnan(bad[2]))
+
+
+def test_moe_small_shapes_and_determinism():
+    for (E, K, N) in [(1, 32, 1), (3, 96, 10), (6, 8192, 33), (2, 15360, 5)]:
+        print(f"moe E={E} K={K} N={N}", flush=True)
+        pool = si.fp4_pool(31, (E, K, N), 4, K, N)
+        d = host.fp4_tensors(pool)
+        ids = np.arange(E, dtype=np.int32)[::-1] % 4
+        x = si.bf16_normal(31, (E, K, N, 7), (E, K))
+        y1 = moe_run(d, x, ids, False)
+        y2 = moe_run(d, x, ids, False)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+        y_ref = oracle.moe_gemv_fp4(x, pool["qw"], pool["s"], ids)
+        W = oracle.dequant_fp4(pool["qw"], pool["s"])
+        for e in range(E):
+            check_outputs(host.bf16_values(y1)[e], y_ref[e], xnorm(x[e]), np.abs(W[ids[e]]).max(axis=1),
+                          f"moe E={E} K={K} N={N} slot {e}")
