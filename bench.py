@@ -4,14 +4,19 @@
 The timed step is one replay of the decode step's HIP graph: 48 layers x 7
 INT4 linears (q 3840->4096, k and v 3840->2048, o 4096->3840, gate and up
 3840->15360, down 15360->3840), group 128, FP16 scale and zero, BF16
-activations, M = 1, every linear reading its own static input.  Inputs are
-seeded synthetic data already resident in device memory.  ``value`` is the
-algorithmic bytes of one step (packed weights + scales + zeros + x + y, each
-once) divided by the measured time per step.
+activations, M = 1, every linear reading its own static input.  The graph
+holds one launch of the persistent decode-chain kernel, which runs the 336
+GEMVs with the decoder's dependencies as stages ({q,k,v} -> {o} ->
+{gate,up} -> {down} per layer).  Inputs are seeded synthetic data already
+resident in device memory.  ``value`` is the algorithmic bytes of one step
+(packed weights + scales + zeros + x + y, each once) divided by the
+measured time per step.
 
 Also reported, outside the timed step:
-  * ``roofline``: the dominant GEMV kernel's own achieved bandwidth, from HIP
-    events around each of its launches on the stream they run on;
+  * ``roofline``: the chain kernel's own achieved bandwidth, from HIP events
+    around each of its launches on the stream it runs on;
+  * ``extra.decode_step_336_launch_graph``: the same step as a graph of 336
+    separate w4_gemv launches, with per-shape kernel timings;
   * ``extra``: the single 3840 x 3840 GEMV, the 262144-row logits GEMV, the
     two M = 128 prefill GEMMs (TFLOP/s) and the six-expert FP4 MoE pair,
     each replayed over rotated weight copies so the data comes from HBM;
@@ -51,8 +56,8 @@ def parse():
 
 
 # ------------------------------------------------------------------ helpers
-def make_decode_step(w4, host, si, torch):
-    from gemm_w4_gemv_amd.decode import DecodeStep
+def decode_linears(host, si, torch):
+    from gemm_w4_gemv_amd.decode import LAYER_STAGE
 
     lins = []
     for layer, idx, name, K, N in si.decode_step_specs():
@@ -61,9 +66,10 @@ def make_decode_step(w4, host, si, torch):
         t["x"] = host.bf16_tensor(x_bits)
         t["y"] = torch.empty(N, dtype=torch.bfloat16, device="cuda")
         t["name"], t["K"], t["N"] = name, K, N
+        t["stage"] = 4 * layer + LAYER_STAGE[name]
         lins.append(t)
     torch.cuda.synchronize()
-    return DecodeStep(lins)
+    return lins
 
 
 def time_graph(torch, replay, stream, reps: int, warmup: int = 2):
@@ -240,12 +246,15 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
 
+    from gemm_w4_gemv_amd.decode import DecodeStep
+
     log("generating and uploading the decode step (336 INT4 linears)")
-    step = make_decode_step(w4, host, si, torch)
-    step_bytes = sum(rf.int4_linear_bytes(l["K"], l["N"]) for l in step.linears)
-    step_flops = sum(rf.flops(1, l["K"], l["N"]) for l in step.linears)
+    lins = decode_linears(host, si, torch)
+    step_bytes = sum(rf.int4_linear_bytes(l["K"], l["N"]) for l in lins)
+    step_flops = sum(rf.flops(1, l["K"], l["N"]) for l in lins)
+    step = DecodeStep(lins, mode="chain")
     step.capture()
-    log("graph captured; warm-up")
+    log(f"chain planned ({step.chain.handle:#x}); graph captured; warm-up")
 
     for _ in range(args.warmup):
         step.replay()
@@ -263,35 +272,56 @@ def main() -> int:
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     gpu_ms_per_step = ev0.elapsed_time(ev1) / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    log(f"decode step: {ms_per_step * 1e3:.1f} us/step (events {gpu_ms_per_step * 1e3:.1f} us), {value:.0f} GB/s")
+    log(f"decode step (chain graph): {ms_per_step * 1e3:.1f} us/step (events {gpu_ms_per_step * 1e3:.1f} us), "
+        f"{value:.0f} GB/s")
+    chain_err = step.chain.error()
+    if chain_err:
+        log(f"chain error word {chain_err:#x}")
+        return 1
 
-    # roofline of the dominant kernel: per-launch events in an eager pass of the same launches
-    durs = per_launch_durations(w4, torch, step)
+    # roofline of the dominant kernel (the chain kernel): an event pair around each launch
+    reps = 20
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(step.stream)
+        step.run_eager()
+        b.record(step.stream)
+    step.stream.synchronize()
+    avg_us = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / reps
+    achieved = step_bytes / (avg_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / rf.HBM_PEAK_GBPS, 4), "traffic": None,
+                "kernel": "chain_kernel (336 INT4 GEMVs, 192 stages, one launch per decode step)",
+                "bytes_per_launch": step_bytes, "avg_launch_us": round(avg_us, 2), "launches_timed": reps}
+    log(f"chain kernel: {avg_us:.1f} us/launch, {achieved:.0f} GB/s")
+    step.destroy()
+
+    # the same step as 336 separate launches
+    extra = {}
+    step2 = DecodeStep(lins, mode="launches")
+    step2.capture()
+    ms2 = time_graph(torch, step2.replay, step2.stream, reps=args.steps, warmup=args.warmup)
+    durs = per_launch_durations(w4, torch, step2)
     by_shape = {}
-    for lin, d in zip(step.linears, durs):
+    for lin, d in zip(lins, durs):
         key = (lin["K"], lin["N"])
         e = by_shape.setdefault(key, {"names": set(), "us": [], "bytes": rf.int4_linear_bytes(*key)})
         e["names"].add(lin["name"])
         e["us"].append(d)
-    dom_key = max(by_shape, key=lambda k: sum(by_shape[k]["us"]))
-    dom = by_shape[dom_key]
-    avg_us = sum(dom["us"]) / len(dom["us"])
-    achieved = dom["bytes"] / (avg_us * 1e-6) / 1e9
-    shapes = {f"{'/'.join(sorted(v['names']))} K{k[0]}->N{k[1]}":
-              {"launches": len(v["us"]), "avg_us": round(sum(v["us"]) / len(v["us"]), 3),
-               "GBps": round(v["bytes"] / (sum(v["us"]) / len(v["us"]) * 1e-6) / 1e9, 1)}
-              for k, v in by_shape.items()}
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / rf.HBM_PEAK_GBPS, 4), "traffic": None,
-                "kernel": f"gemv_int4 ({'/'.join(sorted(dom['names']))} projection, K{dom_key[0]}->N{dom_key[1]})",
-                "bytes_per_launch": dom["bytes"], "avg_launch_us": round(avg_us, 3),
-                "launches_timed": len(dom["us"]), "per_shape": shapes}
-    log(f"dominant kernel {roofline['kernel']}: {avg_us:.2f} us/launch, {achieved:.0f} GB/s")
+    extra["decode_step_336_launch_graph"] = {
+        "us_per_step": round(ms2 * 1e3, 1), "GBps": round(step_bytes / (ms2 * 1e-3) / 1e9, 1),
+        "per_shape_eager_event_us": {f"{'/'.join(sorted(v['names']))} K{k[0]}->N{k[1]}":
+                                     {"launches": len(v["us"]), "avg_us": round(sum(v["us"]) / len(v["us"]), 3),
+                                      "GBps": round(v["bytes"] / (sum(v["us"]) / len(v["us"]) * 1e-6) / 1e9, 1)}
+                                     for k, v in by_shape.items()}}
+    log(f"decode step (336-launch graph): {ms2 * 1e3:.1f} us/step")
+    step2.destroy()
 
-    extra = {}
     if not args.no_extra:
-        extra = extra_workloads(w4, host, si, torch, rf)
-    step.destroy()
+        extra.update(extra_workloads(w4, host, si, torch, rf))
+    n_lins = len(lins)
+    del lins
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -304,8 +334,9 @@ def main() -> int:
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "decode step: one hipGraph replay of 48 layers x 7 INT4 GEMVs "
-                               "(q,k,v,o,gate,up,down; hidden 3840; group 128; M=1)",
-                   "linears": len(step.linears), "bytes_per_step": step_bytes, "flops_per_step": step_flops,
+                               "(q,k,v,o,gate,up,down; hidden 3840; group 128; M=1) run by the persistent "
+                               "chain kernel with stages {q,k,v}->{o}->{gate,up}->{down} per layer",
+                   "linears": n_lins, "stages": 192, "bytes_per_step": step_bytes, "flops_per_step": step_flops,
                    "us_per_step": round(ms_per_step * 1e3, 1), "gpu_us_per_step": round(gpu_ms_per_step * 1e3, 1),
                    "frac_hbm": round(value / rf.HBM_PEAK_GBPS, 4)},
         "roofline": roofline,

@@ -24,12 +24,15 @@ __all__ = [
     "w4_gemv", "w4_gemm", "w4_gemm_workspace_bytes", "w4_moe_gemv",
     "w4_graph_begin", "w4_graph_end", "w4_graph_replay", "w4_graph_destroy", "W4Graph",
     "w4_dequant_int4", "w4_dequant_fp4", "INT4_GROUP", "FP4_GROUP", "GEMV_MAX_K",
+    "GemvDesc", "W4Chain", "w4_chain_workspace_bytes", "w4_chain_create", "w4_chain_run",
+    "w4_chain_error", "w4_chain_destroy", "CHAIN_MAX_K",
 ]
 
 LIB_PATH = pathlib.Path(__file__).resolve().with_name("libw4.so")
 INT4_GROUP = 128
 FP4_GROUP = 32
 GEMV_MAX_K = 32768
+CHAIN_MAX_K = 16384
 
 STATUS = {0: "W4_OK", 1: "W4_ERR_NULL", 2: "W4_ERR_SHAPE", 3: "W4_ERR_UNSUPPORTED", 4: "W4_ERR_ALIGN",
           5: "W4_ERR_WORKSPACE", 6: "W4_ERR_ALIAS", 7: "W4_ERR_ARG", 8: "W4_ERR_HIP"}
@@ -38,6 +41,15 @@ _vp = ctypes.c_void_p
 _i32 = ctypes.c_int
 _i64 = ctypes.c_int64
 _sz = ctypes.c_size_t
+
+
+
+class GemvDesc(ctypes.Structure):
+    """struct w4_gemv_desc (include/w4.h)."""
+    _fields_ = [("x", ctypes.c_void_p), ("qw", ctypes.c_void_p), ("s", ctypes.c_void_p), ("z", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("K", ctypes.c_int), ("N", ctypes.c_int), ("stage", ctypes.c_int),
+                ("reserved", ctypes.c_int)]
+
 
 # name -> (restype, argtypes), mirroring include/w4.h
 SIGNATURES = {
@@ -52,6 +64,11 @@ SIGNATURES = {
     "w4_graph_end": (_i32, [_vp, ctypes.POINTER(_vp)]),
     "w4_graph_replay": (_i32, [_vp, _vp]),
     "w4_graph_destroy": (None, [_vp]),
+    "w4_chain_workspace_bytes": (_sz, [_i32, _i32]),
+    "w4_chain_create": (_i32, [ctypes.POINTER(GemvDesc), _i32, _vp, _sz, ctypes.POINTER(_vp)]),
+    "w4_chain_run": (_i32, [_vp, _vp]),
+    "w4_chain_error": (_i32, [_vp, ctypes.POINTER(ctypes.c_uint32)]),
+    "w4_chain_destroy": (None, [_vp]),
     "w4_dequant_int4": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
     "w4_dequant_fp4": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _vp]),
 }
@@ -229,6 +246,68 @@ def w4_graph_replay(graph: W4Graph, stream=None) -> None:
 
 def w4_graph_destroy(graph: W4Graph) -> None:
     graph.destroy()
+
+
+def w4_chain_workspace_bytes(count: int, num_stages: int) -> int:
+    return lib.w4_chain_workspace_bytes(count, num_stages)
+
+
+class W4Chain:
+    """A planned decode chain (w4_chain_t); keeps its descriptors' tensors alive."""
+
+    def __init__(self, handle: int, keep):
+        self.handle = handle
+        self._keep = keep
+
+    def run(self, stream=None) -> None:
+        w4_chain_run(self, stream)
+
+    def error(self) -> int:
+        return w4_chain_error(self)
+
+    def destroy(self) -> None:
+        if self.handle:
+            lib.w4_chain_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def w4_chain_create(gemvs, workspace: torch.Tensor) -> W4Chain:
+    """Plan a chain.  ``gemvs``: sequence of dicts with device tensors ``x`` (bf16 [K]),
+    ``qw`` (int32 [N, K/8]), ``s``, ``z`` (fp16 [N, K/128]), ``y`` (bf16 [N]) and an int
+    ``stage`` (non-decreasing).  ``workspace``: device tensor of at least
+    w4_chain_workspace_bytes(len(gemvs), number of stages) bytes."""
+    descs = (GemvDesc * len(gemvs))()
+    for i, g in enumerate(gemvs):
+        K = g["x"].numel()
+        N, pq, ps, pz = _int4_weight(g["qw"], g["s"], g["z"], K, INT4_GROUP)
+        if g["y"].numel() != N:
+            raise ValueError(f"gemv {i}: y must hold N = {N} values")
+        descs[i] = GemvDesc(_dev(g["x"], "x", _BF16), pq, ps, pz, _dev(g["y"], "y", _BF16), K, N, int(g["stage"]), 0)
+    nbytes = workspace.numel() * workspace.element_size()
+    h = _vp()
+    _check(lib.w4_chain_create(descs, len(gemvs), _dev(workspace, "workspace", (workspace.dtype,)), nbytes,
+                               ctypes.byref(h)), "w4_chain_create")
+    return W4Chain(h.value, (list(gemvs), workspace))
+
+
+def w4_chain_run(chain: W4Chain, stream=None) -> None:
+    _check(lib.w4_chain_run(chain.handle, _stream(stream)), "w4_chain_run")
+
+
+def w4_chain_error(chain: W4Chain) -> int:
+    word = ctypes.c_uint32(0)
+    _check(lib.w4_chain_error(chain.handle, ctypes.byref(word)), "w4_chain_error")
+    return word.value
+
+
+def w4_chain_destroy(chain: W4Chain) -> None:
+    chain.destroy()
 
 
 def w4_dequant_int4(qw, s, z, out_f32=None, out_bf16=None, group: int = INT4_GROUP, stream=None) -> None:

@@ -1,0 +1,473 @@
+// Persistent decode-chain kernel: a whole sequence of dependent INT4 GEMVs in
+// one launch.
+//
+// "Lab 5: Gemma4 端到端推理优化", sections "CUDA Graph" and "性能分析": once
+// the GEMVs were fused, the decode step's remaining cost was fixed per-launch
+// overhead, so the step is captured and replayed as one unit.  On MI355X a
+// graph node still costs about 1.8 us and every dependent kernel boundary
+// drains and refills HBM (about 4 us of ramp and tail per GEMV), which for a
+// 336-GEMV step is as much time as its 5.7 GB of weights take to stream.  This
+// kernel removes the boundaries; a persistent kernel fusing several GEMMs into
+// one launch is the remedy named in "在 Triton 中利用 Cutlass 内核命名解锁 FP8
+// 张量核心加速" (its last paragraph).
+//
+// The chain is a list of stages.  GEMVs of one stage are independent (q, k, v;
+// gate, up); a GEMV of stage s may read what stages < s wrote.  One 512-thread
+// workgroup runs per compute unit, its waves in two roles:
+//
+//  * Seven compute waves.  The rows of each stage are split evenly over all
+//    compute waves of the GPU.  A wave streams its rows as tiles of 8 chunk
+//    slots per lane (4 rows of K <= 4096, 2 of K <= 8192, 1 of K <= 16384)
+//    through three register sets, so up to three tiles are loading while one
+//    is computed -- across stage boundaries too: weights do not depend on
+//    earlier stages, so HBM keeps streaming while a stage barrier completes.
+//    x comes from LDS.  Outputs are stored with device-coherent (sc1,
+//    write-through) stores.  A wave issues its prefetches after a tile's
+//    stores, so at its last tile of a stage it can wait for exactly its
+//    stores (vmcnt(loads issued since)) before reporting the stage in LDS.
+//    Scale and zero of a slot-row arrive in one load (lanes 0-31 read the
+//    scales, 32-63 the zeros of the segment's 32 groups) and are shuffled
+//    to the lanes that use them: 12 memory instructions per 8 KB tile.
+//  * One control wave.  It stages each stage's x vectors into one of two
+//    LDS buffers, converted once into the dot2 pair layout.  An input that
+//    no earlier stage writes is staged through the caches while the previous
+//    stage still runs; an input written by an earlier stage is staged after
+//    that stage's barrier with device-coherent loads.  It waits until its
+//    compute waves have reported a stage, then announces the workgroup's
+//    progress on its own 128-byte flag line.  The control wave of workgroup
+//    0 also coordinates: it waits for every workgroup's flag and publishes
+//    the stage count on 64 "go" lines, each polled by a few control waves.
+//    All flag accesses are relaxed device-scope atomics; no L2 write-back
+//    or invalidate is ever issued (about 2 us per stage barrier on MI355X,
+//    against 15-90 us for a counter or fence based grid barrier).
+//
+// Compute waves never wait on another wave's memory counter, and the control
+// wave never waits on a weight load.  Every wait is bounded: past the spin
+// limit the waiter records an error in the workspace and leaves, so the
+// launch always ends.
+#include "chain.hpp"
+#include "gemv_common.hpp"
+
+namespace w4 {
+namespace {
+
+// Tile shape.  A tile is 4 slot-rows x 2 chunks per lane.  A row of C <= 128
+// chunks fills one slot-row (4 rows per tile); a longer row is cut into
+// sp = 2 or 4 segments of 128 chunks on consecutive slot-rows (2 or 1 rows
+// per tile), whose partial sums are added after the cross-lane reduction.
+// Slot-row q holds segment (q % sp) of row (q / sp); lane l's chunks in it
+// are 128 (q % sp) + l and + l + 64, in groups 32 (q % sp) + (l + 64 i) / 4.
+constexpr int kSlotRows = 4;
+constexpr int kTileLoads = 3 * kSlotRows;  // 8 weight loads + 4 scale/zero loads per tile
+
+struct TileRegs {
+    u32x4_t w[2 * kSlotRows];  // slot (q, i) in w[2 q + i]
+    uint16_t sz[kSlotRows];    // lane l < 32: scale of group l of the slot-row's segment; l >= 32: zero of l - 32
+};
+
+// A compute wave's position: tile t of stage s, i.e. rows [row, row + nrows)
+// of GEMV g; end = end of the wave's tile range in the stage.
+struct Work {
+    int s, t, end, g, row, nrows;
+};
+
+struct Shared {
+    unsigned x_ready;  // stages whose x is staged and whose predecessors are complete
+    // Stages each compute wave has finished (its stores complete).  One word
+    // per wave, not a shared count: a wave with no tiles in the next stages
+    // reports several at once, and a sum would then run ahead of waves still
+    // working on an earlier stage.
+    unsigned progress[kChainComputeWaves];
+    unsigned abort;
+    unsigned base;
+};
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int seg_shift(int sp) { return sp == 1 ? 0 : (sp == 2 ? 1 : 2); }
+
+__device__ __forceinline__ unsigned lds_load(const unsigned* p) {
+    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ bool older(unsigned a, unsigned b) { return (int)(a - b) < 0; }
+
+__device__ __forceinline__ void set_error(const ChainLaunch& L, Shared& sh, unsigned bit) {
+    __hip_atomic_fetch_or(L.err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&sh.abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Place ``w`` at tile w.t of stage w.s.  Every field is wave-uniform;
+// readfirstlane tells the compiler so, keeping the work state and the buffer
+// descriptors built from it in SGPRs.
+__device__ __forceinline__ void place(const ChainLaunch& L, Work& w) {
+    const ChainStage st = L.stages[w.s];
+    int g = st.gemv0;
+    for (int i = 1; i < st.ngemv; ++i)
+        if (w.t >= L.gemvs[st.gemv0 + i].tile0) g = st.gemv0 + i;
+    g = uniform(g);
+    const ChainGemv& G = L.gemvs[g];
+    const int rpt = kSlotRows / G.sp;
+    w.g = g;
+    w.row = uniform((w.t - G.tile0) * rpt);
+    w.nrows = uniform(min(rpt, G.N - w.row));
+}
+
+// First work at or after stage s for compute wave v of W (s == num_stages:
+// none).  The tiles of a stage are split evenly over the W compute waves.
+__device__ __forceinline__ Work first_from(const ChainLaunch& L, int s, int v, int W) {
+    Work w{};
+    for (; s < L.num_stages; ++s) {
+        const int tiles = L.stages[s].tiles;
+        const int a = uniform((int)(((long long)v * tiles) / W));
+        const int b = uniform((int)(((long long)(v + 1) * tiles) / W));
+        if (a < b) {
+            w.s = uniform(s);
+            w.t = a;
+            w.end = b;
+            place(L, w);
+            return w;
+        }
+    }
+    w.s = uniform(L.num_stages);
+    return w;
+}
+
+__device__ __forceinline__ Work advance(const ChainLaunch& L, Work w, int v, int W) {
+    w.t = uniform(w.t + 1);
+    if (w.t < w.end) {
+        place(L, w);
+        return w;
+    }
+    return first_from(L, w.s + 1, v, W);
+}
+
+// Issue the kTileLoads loads of one tile (no wait).  A dummy issue (past a
+// wave's last tile) repeats w's scale/zero loads and gives its weight loads
+// an empty buffer range, which returns zeros without touching memory: the
+// same loads are issued on every path, so the compiler's wait counts for the
+// first tile stay exact.
+__device__ __forceinline__ void issue(const ChainLaunch& L, const Work& w, bool dummy, int lane, TileRegs& R) {
+    const ChainGemv G = L.gemvs[w.g];
+    const int C = G.C, N = G.N, Gr = C >> 2, sp = G.sp, sh = seg_shift(sp);
+    const uint32_t row_bytes = (uint32_t)C * 16u;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(G.qw, dummy ? 0u : (uint32_t)N * row_bytes);
+#pragma unroll
+    for (int q = 0; q < kSlotRows; ++q) {
+        const uint32_t row = (uint32_t)(w.row + min(q >> sh, w.nrows - 1));
+        const int base = 128 * (q & (sp - 1));
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t c = (uint32_t)min(base + lane + kWave * i, C - 1);
+            R.w[2 * q + i] = buf_load_b128<kAuxNontemporal>(rw, c * 16u, row * row_bytes);
+        }
+    }
+    // A global (not flat) pointer: flat loads would also count in lgkmcnt and
+    // make every LDS wait wait for the prefetches too.
+    typedef __attribute__((address_space(1))) const uint16_t g_u16;
+    g_u16* sz = (g_u16*)(lane < 32 ? G.s : G.z);
+#pragma unroll
+    for (int q = 0; q < kSlotRows; ++q) {
+        const int row = w.row + min(q >> sh, w.nrows - 1);
+        const int grp = min(32 * (q & (sp - 1)) + (lane & 31), Gr - 1);
+        R.sz[q] = sz[(size_t)row * Gr + grp];
+    }
+}
+
+// x of one chunk from the LDS staging buffer: 16 words of dot2 pairs and
+// the chunk sum (chunks past the row end are staged as zeros).
+__device__ __forceinline__ float lds_x_chunk(const unsigned char* xg, int Cp, int c, uint32_t xp[16]) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xg + ((size_t)p * Cp + c) * 16);
+        xp[4 * p + 0] = v.x;
+        xp[4 * p + 1] = v.y;
+        xp[4 * p + 2] = v.z;
+        xp[4 * p + 3] = v.w;
+    }
+    return *reinterpret_cast<const float*>(xg + (size_t)64 * Cp + (size_t)c * 4);
+}
+
+// One slot: chunk (q, i) of the tile, scale/zero shuffled from the slot-row's load.
+__device__ __forceinline__ float slot(const TileRegs& R, int q, int i, int lane, const uint32_t xp[16], float sx,
+                                      uint32_t bias, float acc) {
+    const int gs = (lane + kWave * i) >> 2;  // group within the segment, 0..31
+    const uint16_t sb = (uint16_t)__shfl((int)R.sz[q], gs, kWave);
+    const uint16_t zbits = (uint16_t)__shfl((int)R.sz[q], 32 + gs, kWave);
+    const float d = chunk_dot(R.w[2 * q + i], xp, bias);
+    const float zb = f16_to_f32(zbits) + 128.f;
+    return __builtin_fmaf(f16_to_f32(sb), __builtin_fmaf(-zb, sx, d), acc);
+}
+
+// Compute one tile and store its rows.  ``xg`` is the GEMV's staged x in LDS.
+// With a single segment every row of the tile uses the lane's same two x
+// chunks, read once per tile.
+__device__ __forceinline__ void compute(const ChainGemv& G, const Work& w, int lane, const TileRegs& R,
+                                        const unsigned char* xg) {
+    const int sp = G.sp, Cp = chain_x_chunks(G.C);
+    const uint32_t bias = vgpr_const(kInt4BiasPair);
+    float acc[kSlotRows];
+    // Slot-row q reads segment q mod sp of its row.  Chunk column i of every
+    // slot-row first: with one segment the x chunk read for q = 0 serves all
+    // four rows, and only one chunk of x is held at a time.
+#pragma unroll
+    for (int q = 0; q < kSlotRows; ++q) acc[q] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        uint32_t xp[16];
+        float sx = 0.f;
+#pragma unroll
+        for (int q = 0; q < kSlotRows; ++q) {
+            if (q == 0 || sp > 1) sx = lds_x_chunk(xg, Cp, 128 * (q & (sp - 1)) + lane + kWave * i, xp);
+            acc[q] = slot(R, q, i, lane, xp, sx, bias, acc[q]);
+            // One slot's x at a time: hoisted LDS reads would need more VGPRs
+            // than the two tile register sets leave.
+            asm volatile("" : "+v"(acc[q])::"memory");
+        }
+    }
+    float total = reduce_rows<kSlotRows>(acc, lane);  // lane L: slot-row L / 16
+    if (sp >= 2) total += __shfl_xor(total, 16, kWave);
+    if (sp == 4) total += __shfl_xor(total, 32, kWave);
+    const int j = (lane >> 4) >> seg_shift(sp);  // row of the tile this lane's total belongs to
+    if ((lane & (16 * sp - 1)) == 0 && j < w.nrows) {
+        const __amdgpu_buffer_rsrc_t ry = make_rsrc(G.y, (uint32_t)G.N * 2u);
+        buf_store_u16_coherent(f32_to_bf16(total), ry, (uint32_t)(w.row + j) * 2u, 0);
+    }
+}
+
+// --------------------------------------------------------------- control wave
+constexpr int kStageBatch = 4;  // slots of 64 x chunks loaded at once when staging x
+
+// Slot ``k`` of a stage's x staging: chunks [64 m, 64 m + 64) of GEMV g
+// (slots cover each GEMV's padded chunk count).
+__device__ __forceinline__ bool stage_slot(const ChainLaunch& L, const ChainStage& st, int k, int& g, int& m) {
+    for (int gi = 0; gi < st.ngemv; ++gi) {
+        const int n = chain_x_chunks(L.gemvs[st.gemv0 + gi].C) / kWave;
+        if (k < n) {
+            g = uniform(st.gemv0 + gi);
+            m = uniform(k);
+            return true;
+        }
+        k -= n;
+    }
+    return false;
+}
+
+__device__ __forceinline__ int stage_slots(const ChainLaunch& L, const ChainStage& st) {
+    int n = 0;
+    for (int gi = 0; gi < st.ngemv; ++gi) n += chain_x_chunks(L.gemvs[st.gemv0 + gi].C) / kWave;
+    return n;
+}
+
+// Staging of a stage's x into an LDS buffer, in batches of kStageBatch slots:
+// bf16 pairs in the dot2 order (word p of chunk c at 16 (p Cp + c)), then the
+// chunk sums; padding chunks are zeros.  issue() only loads (inputs written
+// by an earlier stage device-coherently), so the loads can be in flight while
+// the wave waits; finish() converts and writes.
+struct XBatch {
+    u32x4_t raw[kStageBatch][4];
+};
+
+__device__ __forceinline__ void stage_issue(const ChainLaunch& L, const ChainStage& st, int b0, int lane, XBatch& B) {
+#pragma unroll
+    for (int j = 0; j < kStageBatch; ++j) {
+        int g, m;
+        if (!stage_slot(L, st, b0 + j, g, m)) break;
+        const ChainGemv& G = L.gemvs[g];
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(G.x, (uint32_t)G.C * 64u);
+        const uint32_t c = (uint32_t)min(m * kWave + lane, G.C - 1);
+        if (G.x_internal) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) B.raw[j][p] = buf_load_b128_coherent(rx, c * 64u + 16u * p, 0);
+        } else {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) B.raw[j][p] = buf_load_b128<0>(rx, c * 64u + 16u * p, 0);
+        }
+    }
+}
+
+__device__ __forceinline__ void stage_finish(const ChainLaunch& L, const ChainStage& st, int b0, int lane,
+                                             const XBatch& B, unsigned char* xb) {
+#pragma unroll
+    for (int j = 0; j < kStageBatch; ++j) {
+        int g, m;
+        if (!stage_slot(L, st, b0 + j, g, m)) break;
+        const ChainGemv& G = L.gemvs[g];
+        const int C = G.C, Cp = chain_x_chunks(C), c = m * kWave + lane;
+        unsigned char* xg = xb + G.x_lds;
+        uint32_t xp[16];
+        float sum = 0.f;
+        if (c < C) {
+            sum = x_chunk_pairs(B.raw[j], xp);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) xp[k] = 0u;
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            *reinterpret_cast<u32x4_t*>(xg + ((size_t)p * Cp + c) * 16) =
+                u32x4_t{xp[4 * p], xp[4 * p + 1], xp[4 * p + 2], xp[4 * p + 3]};
+        *reinterpret_cast<float*>(xg + (size_t)64 * Cp + (size_t)c * 4) = sum;
+    }
+}
+
+// Whole staging of stage s (all batches, loads then writes per batch).
+__device__ void stage_x(const ChainLaunch& L, int s, unsigned char* xb, int lane) {
+    const ChainStage st = L.stages[s];
+    const int n = stage_slots(L, st);
+    for (int b0 = 0; b0 < n; b0 += kStageBatch) {
+        XBatch B;
+        stage_issue(L, st, b0, lane, B);
+        stage_finish(L, st, b0, lane, B, xb);
+    }
+}
+
+__device__ void control_wave(const ChainLaunch& L, Shared& sh, unsigned char* xl, int lane) {
+    const int wg = blockIdx.x, P = L.workers;
+    unsigned* my_flag = L.flags + (size_t)wg * kChainLineWords;
+    const unsigned* my_go = L.go + (size_t)(wg % kChainGoLines) * kChainLineWords;
+    const unsigned base = sh.base;
+    stage_x(L, 0, xl, lane);
+    __hip_atomic_store(&sh.x_ready, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int s = 0; s < L.num_stages; ++s) {
+        const bool more = s + 1 < L.num_stages;
+        unsigned char* xnext = xl + (size_t)((s + 1) & 1) * kChainXLdsBytes;
+        // Inputs of the next stage that no stage writes are staged now, while
+        // the compute waves work on stage s: the buffer held stage s - 1's x,
+        // which this workgroup's compute waves are done with.  Only their
+        // release waits for the barrier.
+        const bool early = more && !L.stages[s + 1].x_internal;
+        if (early) stage_x(L, s + 1, xnext, lane);
+
+        // Every compute wave of this workgroup has finished stage s (stores complete).
+        unsigned n = 0;
+        while (__builtin_amdgcn_ballot_w64(lane < kChainComputeWaves &&
+                                           lds_load(&sh.progress[lane < kChainComputeWaves ? lane : 0]) <=
+                                               (unsigned)s) != 0) {
+            if (lds_load(&sh.abort) || ++n > L.spin_limit) { set_error(L, sh, 4u); return; }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        const unsigned target = base + (unsigned)s + 1u;
+        if (lane == 0) flag_store(my_flag, target);
+        if (!more) break;  // nothing waits for the last stage
+
+        if (wg == 0) {  // coordinator: every workgroup's stage s, then publish
+            for (int w = lane; w < P; w += kWave) {
+                unsigned m = 0;
+                while (older(flag_load(L.flags + (size_t)w * kChainLineWords), target)) {
+                    if (++m > L.spin_limit) { set_error(L, sh, 1u); break; }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            if (lds_load(&sh.abort)) return;
+            if (lane < kChainGoLines) flag_store(L.go + (size_t)lane * kChainLineWords, target);
+        }
+        n = 0;
+        while (older(flag_load(my_go), target)) {
+            if (++n > L.spin_limit) { set_error(L, sh, 2u); return; }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (!early) stage_x(L, s + 1, xnext, lane);
+        __hip_atomic_store(&sh.x_ready, (unsigned)s + 2u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+}
+
+// --------------------------------------------------------------- compute wave
+__device__ void compute_wave(const ChainLaunch& L, Shared& sh, const unsigned char* xl, int lane, int wi, int v,
+                             int W) {
+    // Report stages < upto done; the caller has made its stores complete.
+    auto report = [&](int upto) {
+        if (lane == 0)
+            __hip_atomic_store(&sh.progress[wi], (unsigned)upto, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    // Wait until stage s's x is staged.  On abort or time-out the wave goes on
+    // without waiting (the outputs are then undefined; the error word says
+    // so): leaving the tile loop early instead makes the compiler's wait-count
+    // analysis assume that the prefetched tiles were issued last, and wait for
+    // all of them before every tile's math.
+    auto wait_x = [&](int s) {
+        unsigned n = 0, r = lds_load(&sh.x_ready), ab = lds_load(&sh.abort);
+        while ((r <= (unsigned)s) & (ab == 0u) & (n <= L.spin_limit)) {
+            __builtin_amdgcn_s_sleep(1);
+            ++n;
+            r = lds_load(&sh.x_ready);
+            ab = lds_load(&sh.abort);
+        }
+    };
+
+    Work a = first_from(L, 0, v, W);
+    report(a.s);  // no tiles in the first a.s stages; nothing pending
+    int x_stage = -1;  // stage whose x this workgroup has staged and released
+
+    // Compute the tile w (its loads in R); then, if nxt is in a later stage,
+    // wait for the stores and report w's stage done.
+    auto run = [&](const Work& w, const TileRegs& R, const Work& nxt) {
+        if (x_stage != w.s) {
+            wait_x(w.s);
+            x_stage = w.s;
+        }
+        const ChainGemv G = L.gemvs[w.g];
+        compute(G, w, lane, R, xl + (size_t)(w.s & 1) * kChainXLdsBytes + G.x_lds);
+        if (nxt.s != w.s) {
+            __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's stores are complete
+            report(nxt.s);
+        }
+    };
+
+    // Two tiles per iteration, both loaded before either is computed (and
+    // before any wait for x, so the loads overlap the stage barrier).  Nothing
+    // stays in flight from one iteration to the next, so the compiler's own
+    // wait counts are exact; latency is hidden by the other compute waves.
+    // Past the last tile the second issue is a dummy (empty buffer range).
+    while (a.s < L.num_stages) {
+        const Work b = advance(L, a, v, W);
+        const bool has_b = b.s < L.num_stages;
+        TileRegs RA, RB;
+        issue(L, a, false, lane, RA);
+        issue(L, has_b ? b : a, !has_b, lane, RB);
+        run(a, RA, b);
+        if (!has_b) break;
+        const Work c = advance(L, b, v, W);
+        run(b, RB, c);
+        a = c;
+    }
+}
+
+__global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainStage* __restrict__ stages,
+                                                            const ChainGemv* __restrict__ gemvs, ChainLaunch L) {
+    // The tables are read-only for the whole launch; as restrict kernel
+    // arguments the compiler reads them with scalar loads, which do not
+    // count in vmcnt (a vector load here would wait for every prefetch).
+    L.stages = stages;
+    L.gemvs = gemvs;
+    __shared__ __attribute__((aligned(16))) unsigned char xl[2 * kChainXLdsBytes];
+    __shared__ Shared sh;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    if (tid == 0) {
+        sh.x_ready = 0;
+        for (int i = 0; i < kChainComputeWaves; ++i) sh.progress[i] = 0;
+        sh.abort = 0;
+        sh.base = flag_load(L.flags + (size_t)blockIdx.x * kChainLineWords);
+    }
+    __syncthreads();  // the only workgroup barrier: roles split below
+    if (wave == 0) {
+        control_wave(L, sh, xl, lane);
+    } else {
+        const int W = L.workers * kChainComputeWaves;
+        compute_wave(L, sh, xl, lane, wave - 1, uniform((int)blockIdx.x * kChainComputeWaves + (wave - 1)), W);
+    }
+}
+
+}  // namespace
+
+hipError_t chain_occupancy(int* blocks_per_cu) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, chain_kernel, kChainThreads, 0);
+}
+
+hipError_t launch_chain(const ChainLaunch& l, hipStream_t stream) {
+    chain_kernel<<<l.workers, kChainThreads, 0, stream>>>(l.stages, l.gemvs, l);
+    return hipGetLastError();
+}
+
+}  // namespace w4

@@ -1,0 +1,83 @@
+// Tables of the persistent decode-chain kernel, shared by the host planner
+// (w4_api.hip) and the kernel (chain.hip).  They live in the caller's
+// workspace, written once by w4_chain_create.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4 {
+
+// One INT4 GEMV of the chain.
+struct ChainGemv {
+    const void* qw;  // int32 [N][K/8]
+    const void* s;   // fp16 [N][K/128]
+    const void* z;   // fp16 [N][K/128]
+    const void* x;   // bf16 [K]
+    void* y;         // bf16 [N]
+    int C;           // K / 32 chunks of 16 bytes per row
+    int N;
+    int sp;          // segments of 128 chunks per row: 1 (K <= 4096), 2 (K <= 8192) or 4 (K <= 16384)
+    int tile0;       // first tile of this GEMV in its stage (tiles are 4 / sp rows)
+    int x_lds;       // byte offset of this GEMV's staged x in its LDS buffer
+    int x_internal;  // 1: x is written by an earlier stage of the chain
+};
+
+// GEMVs gemv0 .. gemv0 + ngemv - 1 form one stage: they run concurrently;
+// every one of them starts after all earlier stages have written their outputs.
+struct ChainStage {
+    int gemv0;
+    int ngemv;
+    int tiles;       // total tiles of the stage's GEMVs
+    int x_internal;  // 1: some input of the stage is written by an earlier stage
+};
+
+constexpr int kChainThreads = 1024;  // 16 waves: 1 control + 15 compute
+constexpr int kChainComputeWaves = 15;
+constexpr int kChainMaxWorkers = 1024;
+constexpr int kChainGoLines = 64;
+constexpr int kChainLineWords = 32;    // one 128-byte line per flag
+constexpr int kChainMaxC = 512;        // K <= 16384
+constexpr int kChainXLdsBytes = 65536; // staged x (pairs + chunk sums) of one stage; two buffers
+constexpr int kChainSlots = 8;         // chunk slots per lane per tile
+
+// Staged x of one GEMV is zero-padded to whole segments of 128 chunks, so
+// the kernel never masks a chunk index.
+__host__ __device__ inline int chain_x_chunks(int C) { return (C + 127) / 128 * 128; }
+// Bytes of LDS one GEMV's staged x takes: 64 bytes of bf16 pairs and one
+// FP32 sum per (padded) chunk.
+__host__ __device__ inline int chain_x_lds_bytes(int C) { return 68 * chain_x_chunks(C); }
+
+// Workspace layout: [error line][worker flag lines][go lines][stages][gemvs].
+struct ChainLayout {
+    size_t err, flags, go, stages, gemvs, total;
+};
+
+inline ChainLayout chain_layout(int num_gemvs, int num_stages) {
+    const size_t line = kChainLineWords * 4;
+    ChainLayout l;
+    l.err = 0;
+    l.flags = line;
+    l.go = l.flags + (size_t)kChainMaxWorkers * line;
+    l.stages = l.go + (size_t)kChainGoLines * line;
+    l.gemvs = l.stages + (size_t)num_stages * sizeof(ChainStage);
+    l.gemvs = (l.gemvs + 63) & ~(size_t)63;
+    l.total = l.gemvs + (size_t)num_gemvs * sizeof(ChainGemv);
+    return l;
+}
+
+struct ChainLaunch {
+    const ChainStage* stages;
+    const ChainGemv* gemvs;
+    unsigned* err;
+    unsigned* flags;
+    unsigned* go;
+    int num_stages;
+    int workers;  // workgroups, one per compute unit
+    unsigned spin_limit;
+};
+
+hipError_t launch_chain(const ChainLaunch& l, hipStream_t stream);
+hipError_t chain_occupancy(int* blocks_per_cu);
+
+}  // namespace w4

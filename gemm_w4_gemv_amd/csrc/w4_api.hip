@@ -6,6 +6,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
+#include "chain.hpp"
 #include "w4.h"
 #include "w4_internal.hpp"
 
@@ -198,6 +201,141 @@ W4_API void w4_graph_destroy(w4_graph_t graph) {
     (void)hipGraphDestroy(graph->graph);
     delete graph;
 }
+
+// ------------------------------------------------------------ decode chains
+struct w4_chain {
+    w4::ChainLaunch launch;
+};
+
+W4_API size_t w4_chain_workspace_bytes(int count, int num_stages) {
+    if (count <= 0 || num_stages <= 0) return 0;
+    return w4::chain_layout(count, num_stages).total;
+}
+
+W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* workspace, size_t workspace_bytes,
+                                 w4_chain_t* chain) {
+    const char* fn = "w4_chain_create";
+    if (!chain) return fail(W4_ERR_ARG, "%s: chain must not be NULL", fn);
+    *chain = nullptr;
+    if (!descs || !workspace) return fail(W4_ERR_NULL, "%s: descs and workspace must not be NULL", fn);
+    if (count <= 0) return fail(W4_ERR_ARG, "%s: count = %d must be positive", fn, count);
+    if (!aligned(workspace, 256)) return fail(W4_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+    std::vector<Range> writes(count), reads(count), weights;
+    int num_stages = 0;
+    for (int i = 0; i < count; ++i) {
+        const w4_gemv_desc& d = descs[i];
+        if (!d.x || !d.y) return fail(W4_ERR_NULL, "%s: descriptor %d: x and y must not be NULL", fn, i);
+        w4_status st = check_int4(fn, d.qw, d.s, d.z, d.K, d.N, W4_INT4_GROUP, W4_CHAIN_MAX_K);
+        if (st != W4_OK) return st;
+        if (!aligned(d.x, 16) || !aligned(d.y, 2)) return fail(W4_ERR_ALIGN, "%s: descriptor %d: x or y misaligned", fn, i);
+        if (d.reserved != 0) return fail(W4_ERR_ARG, "%s: descriptor %d: reserved must be 0", fn, i);
+        if (d.stage < 0 || (i > 0 && d.stage < descs[i - 1].stage))
+            return fail(W4_ERR_ARG, "%s: descriptor %d: stages must be non-negative and non-decreasing", fn, i);
+        if (i == 0 || d.stage != descs[i - 1].stage) ++num_stages;
+        const size_t sz = (size_t)d.N * (d.K / W4_INT4_GROUP) * 2;
+        writes[i] = range(d.y, (size_t)d.N * 2);
+        reads[i] = range(d.x, (size_t)d.K * 2);
+        weights.push_back(range(d.qw, (size_t)d.N * d.K / 2));
+        weights.push_back(range(d.s, sz));
+        weights.push_back(range(d.z, sz));
+    }
+    for (int i = 0; i < count; ++i) {
+        for (const Range& w : weights)
+            if (overlap(writes[i], w)) return fail(W4_ERR_ALIAS, "%s: output %d overlaps a weight, scale or zero", fn, i);
+        for (int j = 0; j < count; ++j) {
+            if (j != i && overlap(writes[i], writes[j])) return fail(W4_ERR_ALIAS, "%s: outputs %d and %d overlap", fn, i, j);
+            if (descs[j].stage == descs[i].stage && overlap(writes[i], reads[j]))
+                return fail(W4_ERR_ALIAS, "%s: output %d overlaps input %d of the same stage", fn, i, j);
+        }
+    }
+    const w4::ChainLayout lay = w4::chain_layout(count, num_stages);
+    if (workspace_bytes < lay.total)
+        return fail(W4_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, lay.total, workspace_bytes);
+    for (int i = 0; i < count; ++i)
+        if (overlap(range(workspace, lay.total), writes[i]) || overlap(range(workspace, lay.total), reads[i]))
+            return fail(W4_ERR_ALIAS, "%s: workspace overlaps descriptor %d", fn, i);
+    for (const Range& w : weights)
+        if (overlap(range(workspace, lay.total), w)) return fail(W4_ERR_ALIAS, "%s: workspace overlaps a weight", fn);
+
+    // Tables.
+    std::vector<w4::ChainStage> stages;
+    std::vector<w4::ChainGemv> gemvs(count);
+    int x_bytes = 0;
+    for (int i = 0; i < count; ++i) {
+        const w4_gemv_desc& d = descs[i];
+        if (i == 0 || d.stage != descs[i - 1].stage) {
+            stages.push_back({i, 0, 0, 0});
+            x_bytes = 0;
+        }
+        w4::ChainStage& st = stages.back();
+        w4::ChainGemv& g = gemvs[i];
+        g.qw = d.qw;
+        g.s = d.s;
+        g.z = d.z;
+        g.x = d.x;
+        g.y = d.y;
+        g.C = d.K / 32;
+        g.N = d.N;
+        g.sp = g.C <= 128 ? 1 : (g.C <= 256 ? 2 : 4);
+        g.tile0 = st.tiles;
+        g.x_lds = x_bytes;
+        g.x_internal = 0;
+        for (int j = 0; j < i && !g.x_internal; ++j)
+            if (descs[j].stage < d.stage && overlap(writes[j], reads[i])) g.x_internal = 1;
+        st.x_internal |= g.x_internal;
+        x_bytes += w4::chain_x_lds_bytes(g.C);
+        if (x_bytes > w4::kChainXLdsBytes)
+            return fail(W4_ERR_SHAPE, "%s: the inputs of stage %d need %d bytes of LDS (limit %d)",
+                        fn, d.stage, x_bytes, w4::kChainXLdsBytes);
+        const int rows_per_tile = 4 / g.sp;
+        st.tiles += (d.N + rows_per_tile - 1) / rows_per_tile;
+        st.ngemv += 1;
+    }
+    int occ = 0, cus = 0, dev = 0;
+    hipError_t err = w4::chain_occupancy(&occ);
+    if (err == hipSuccess) err = hipGetDevice(&dev);
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return hip_fail(err, "w4_chain_create (device query)");
+    if (occ < 1) return fail(W4_ERR_HIP, "%s: the chain kernel cannot be resident (occupancy %d)", fn, occ);
+    int workers = cus;  // one workgroup per compute unit, all resident at once
+    if (workers > w4::kChainMaxWorkers) workers = w4::kChainMaxWorkers;
+
+    char* base = static_cast<char*>(workspace);
+    err = hipMemset(base, 0, lay.stages);
+    if (err == hipSuccess)
+        err = hipMemcpy(base + lay.stages, stages.data(), stages.size() * sizeof(w4::ChainStage), hipMemcpyHostToDevice);
+    if (err == hipSuccess)
+        err = hipMemcpy(base + lay.gemvs, gemvs.data(), gemvs.size() * sizeof(w4::ChainGemv), hipMemcpyHostToDevice);
+    if (err == hipSuccess) err = hipDeviceSynchronize();
+    if (err != hipSuccess) return hip_fail(err, "w4_chain_create (upload)");
+
+    w4::ChainLaunch L;
+    L.stages = reinterpret_cast<const w4::ChainStage*>(base + lay.stages);
+    L.gemvs = reinterpret_cast<const w4::ChainGemv*>(base + lay.gemvs);
+    L.err = reinterpret_cast<unsigned*>(base + lay.err);
+    L.flags = reinterpret_cast<unsigned*>(base + lay.flags);
+    L.go = reinterpret_cast<unsigned*>(base + lay.go);
+    L.num_stages = num_stages;
+    L.workers = workers;
+    L.spin_limit = 1u << 20;
+    *chain = new w4_chain{L};
+    return W4_OK;
+}
+
+W4_API w4_status w4_chain_run(w4_chain_t chain, void* stream) {
+    if (!chain) return fail(W4_ERR_ARG, "w4_chain_run: chain must not be NULL");
+    hipError_t err = w4::launch_chain(chain->launch, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4_OK : hip_fail(err, "w4_chain_run");
+}
+
+W4_API w4_status w4_chain_error(w4_chain_t chain, uint32_t* error_word) {
+    if (!chain || !error_word) return fail(W4_ERR_ARG, "w4_chain_error: chain and error_word must not be NULL");
+    hipError_t err = hipDeviceSynchronize();
+    if (err == hipSuccess) err = hipMemcpy(error_word, chain->launch.err, sizeof(uint32_t), hipMemcpyDeviceToHost);
+    return err == hipSuccess ? W4_OK : hip_fail(err, "w4_chain_error");
+}
+
+W4_API void w4_chain_destroy(w4_chain_t chain) { delete chain; }
 
 W4_API w4_status w4_dequant_int4(const int32_t* qw, const void* s, const void* z, float* out_f32,
                                  void* out_bf16, int K, int N, int g, void* stream) {

@@ -24,17 +24,46 @@ constexpr int kWave = 64;
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kAuxNontemporal = 2;  // stream past the caches: read once
 
+// The base, size and SGPR offset of a buffer access are wave-uniform by
+// contract; readfirstlane states it to the compiler (free when the value is
+// already scalar), so descriptors never need a per-lane waterfall loop.
+__device__ __forceinline__ uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint64_t u = ((uint64_t)sgpr((uint32_t)(b >> 32)) << 32) | sgpr((uint32_t)b);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), (short)0, (int)sgpr(bytes), kBufferWord3);
 }
 
 template <int kAux = 0>
 __device__ __forceinline__ u32x4_t buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kAux));
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)sgpr(soff), kAux));
 }
 
 __device__ __forceinline__ uint16_t buf_load_u16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)sgpr(soff), 0);
+}
+
+// Device-coherent access (cache policy sc1): loads miss in an XCD's
+// non-coherent L2 lines and stores write through, so data exchanged between
+// workgroups on different XCDs needs no L2 write-back or invalidate.
+constexpr int kAuxDeviceCoherent = 16;
+
+__device__ __forceinline__ u32x4_t buf_load_b128_coherent(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4_t,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)sgpr(soff), kAuxDeviceCoherent));
+}
+
+__device__ __forceinline__ void buf_store_u16_coherent(uint16_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)voff, (int)sgpr(soff), kAuxDeviceCoherent);
+}
+
+// Relaxed device-scope flag access (vector loads/stores with sc1; no fences).
+__device__ __forceinline__ unsigned flag_load(const unsigned* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void flag_store(unsigned* p, unsigned v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ formats

@@ -1,5 +1,13 @@
 """The decode step's GEMV chain captured once into a HIP graph.
 
+Two ways to run the step are offered:
+
+* ``launches``: one ``w4_gemv`` launch per linear (336 graph nodes);
+* ``chain``: one ``w4_chain_run`` launch (a single graph node) of the
+  persistent chain kernel, with the decoder's dependencies as stages:
+  per layer {q, k, v} -> {o} -> {gate, up} -> {down}, each stage starting
+  after the previous one has written its outputs.
+
 "Lab 5: Gemma4 端到端推理优化", section "CUDA Graph": after the fused GEMV the
 remaining cost was launch and Python overhead, so the whole decode step is
 captured once into a static graph and replayed once per token; the graph
@@ -12,7 +20,16 @@ from __future__ import annotations
 
 import torch
 
-from . import w4_gemv, w4_graph_begin, w4_graph_end, W4Graph
+from . import w4_gemv, w4_graph_begin, w4_graph_end, W4Graph, w4_chain_create, w4_chain_run, \
+    w4_chain_workspace_bytes
+
+# stage of each decoder linear within its layer: {q, k, v} -> {o} -> {gate, up} -> {down}
+LAYER_STAGE = {"q": 0, "k": 0, "v": 0, "o": 1, "gate": 2, "up": 2, "down": 3}
+
+
+def decoder_stages(names, layers_of):
+    """Stage number of every linear, from its name and layer index."""
+    return [4 * layer + LAYER_STAGE[name] for name, layer in zip(names, layers_of)]
 
 
 class DecodeStep:
@@ -23,13 +40,26 @@ class DecodeStep:
     ``y`` (bfloat16 [N]).  The tensors must stay alive while the graph does.
     """
 
-    def __init__(self, linears, stream: torch.cuda.Stream | None = None):
+    def __init__(self, linears, stream: torch.cuda.Stream | None = None, mode: str = "launches"):
+        if mode not in ("launches", "chain"):
+            raise ValueError("mode must be 'launches' or 'chain'")
         self.linears = list(linears)
         self.stream = stream if stream is not None else torch.cuda.Stream()
+        self.mode = mode
         self.graph: W4Graph | None = None
+        self.chain = None
+        if mode == "chain":
+            stages = [lin["stage"] for lin in self.linears]
+            nbytes = w4_chain_workspace_bytes(len(stages), len(set(stages)))
+            self.workspace = torch.zeros(nbytes + 256, dtype=torch.uint8, device="cuda")
+            off = (-self.workspace.data_ptr()) % 256
+            self.chain = w4_chain_create(self.linears, self.workspace[off:off + nbytes])
 
     def run_eager(self) -> None:
-        """Launch the chain directly on the step's stream (no graph)."""
+        """Run the step directly on the step's stream (no graph)."""
+        if self.mode == "chain":
+            w4_chain_run(self.chain, stream=self.stream)
+            return
         for lin in self.linears:
             w4_gemv(lin["x"], lin["qw"], lin["s"], lin["z"], lin["y"], stream=self.stream)
 
@@ -56,3 +86,6 @@ class DecodeStep:
         if self.graph is not None:
             self.graph.destroy()
             self.graph = None
+        if self.chain is not None:
+            self.chain.destroy()
+            self.chain = None

@@ -165,6 +165,64 @@ W4_API w4_status w4_graph_replay(w4_graph_t graph, void* stream);
 W4_API void w4_graph_destroy(w4_graph_t graph);
 
 /*
+ * Decode chains: a sequence of dependent INT4 GEMVs run by one persistent
+ * launch.  "Lab 5: Gemma4 端到端推理优化", sections "CUDA Graph" and "性能分析":
+ * after fusing the GEMV, the decode step's remaining cost is per-launch
+ * overhead; "在 Triton 中利用 Cutlass 内核命名解锁 FP8 张量核心加速" (last
+ * paragraph) names the remedy, a persistent kernel that fuses several GEMMs
+ * into one launch.
+ *
+ * Each descriptor is one w4_gemv (same operands, layouts and limits, plus
+ * K <= W4_CHAIN_MAX_K) tagged with a stage number.  Descriptors must be given
+ * in non-decreasing stage order.  GEMVs of one stage may run in any order or
+ * concurrently; every GEMV of a later stage starts after every GEMV of the
+ * earlier stages has written its output, so a later stage may read (as x)
+ * what an earlier stage wrote (as y).  An output must not overlap any
+ * weight, scale or zero of the chain, any other output, or any input of its
+ * own stage.  The x vectors of one stage must fit the kernel's LDS staging
+ * area: the sum over the stage's GEMVs of 68 * ceil(K / 4096) * 128 bytes
+ * at most 65536 (W4_ERR_SHAPE otherwise).
+ *
+ * w4_chain_create validates the descriptors on the host, then (blocking, not
+ * capturable) zeroes the synchronisation words of ``workspace`` and writes
+ * the chain's tables into it; it never allocates device memory.  The
+ * workspace (device memory, 256-byte aligned, at least
+ * w4_chain_workspace_bytes(count, count) bytes) belongs to the chain until
+ * w4_chain_destroy.  w4_chain_run enqueues one run on ``stream`` (one kernel
+ * launch; capturable into a graph).  Runs of one chain must not overlap each
+ * other or any other kernel that fills the GPU: the launch keeps one
+ * workgroup resident on every compute unit and they wait for each other.  Every
+ * wait is bounded: a run that cannot make progress ends within about a
+ * second and records a non-zero error word; w4_chain_error synchronises the
+ * device and returns that word (0 = no error).  After a non-zero error word,
+ * create the chain again before running it.
+ * Errors: W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_UNSUPPORTED, W4_ERR_ALIGN,
+ * W4_ERR_ALIAS, W4_ERR_ARG (no descriptors, stage order), W4_ERR_WORKSPACE,
+ * W4_ERR_HIP.
+ */
+#define W4_CHAIN_MAX_K 16384
+
+typedef struct w4_gemv_desc {
+    const void* x;     /* device bf16 [K], 16-byte aligned */
+    const int32_t* qw; /* device int32 [N][K/8], 16-byte aligned */
+    const void* s;     /* device fp16 [N][K/128] */
+    const void* z;     /* device fp16 [N][K/128] */
+    void* y;           /* device bf16 [N] */
+    int K;
+    int N;
+    int stage;
+    int reserved;      /* must be 0 */
+} w4_gemv_desc;
+
+typedef struct w4_chain* w4_chain_t;
+W4_API size_t w4_chain_workspace_bytes(int count, int num_stages);
+W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* workspace,
+                                 size_t workspace_bytes, w4_chain_t* chain);
+W4_API w4_status w4_chain_run(w4_chain_t chain, void* stream);
+W4_API w4_status w4_chain_error(w4_chain_t chain, uint32_t* error_word);
+W4_API void w4_chain_destroy(w4_chain_t chain);
+
+/*
  * Test-only dequantisers, sharing the device unpack code of the GEMM and the
  * FP4 GEMV.  They write the FP32 value of every weight (exact: at most 15
  * significant bits) and/or its BF16 round-to-nearest-even, so the packed

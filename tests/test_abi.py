@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 18, names
     for name in names:
         assert hasattr(lib, name), f"libw4.so does not export {name}"
         assert name in w4.SIGNATURES, f"binding has no signature for {name}"
@@ -144,3 +144,37 @@ def test_byte_model_against_pages():
     gap = lambda v: abs(v - g["pages_bytes"])
     assert gap(total) < gap(scale_only) and gap(total) < gap(packed_zero)
     assert round(g["pages_bytes"] / 2 ** 30, 3) == g["pages_gib"]
+
+
+def test_chain_validation():
+    def desc(**k):
+        d = dict(x=X, qw=QW, s=S, z=Z, y=Y, K=3840, N=4096, stage=0, reserved=0)
+        d.update(k)
+        return w4.GemvDesc(d["x"], d["qw"], d["s"], d["z"], d["y"], d["K"], d["N"], d["stage"], d["reserved"])
+
+    def create(descs, ws=WSP, nbytes=1 << 20):
+        arr = (w4.GemvDesc * len(descs))(*descs)
+        h = ctypes.c_void_p()
+        st = lib.w4_chain_create(arr, len(descs), ws, nbytes, ctypes.byref(h))
+        assert h.value is None
+        return st
+
+    assert lib.w4_chain_workspace_bytes(336, 192) > 128 * 1024
+    assert lib.w4_chain_workspace_bytes(0, 1) == 0
+    assert create([desc()], ws=None) == NULL
+    assert create([desc(K=16384 + 128)]) == SHAPE          # the chain's K limit
+    assert create([desc(K=100)]) == SHAPE
+    assert create([desc(x=X + 8)]) == ALIGN
+    assert create([desc()], ws=WSP + 128) == ALIGN           # workspace needs 256-byte alignment
+    assert create([desc(reserved=1)]) == ARG
+    assert create([desc(stage=1), desc(stage=0, y=Y + 65536)]) == ARG   # stages must not decrease
+    assert create([desc(stage=-1)]) == ARG
+    assert create([desc(), desc(y=Y + 2)]) == ALIAS          # two outputs overlap
+    assert create([desc(y=QW + 64)]) == ALIAS                 # output over a weight
+    assert create([desc(), desc(x=Y, y=Y + 65536)]) == ALIAS  # same-stage read of an output
+    assert create([desc()], nbytes=64) == WS
+    h = ctypes.c_void_p()
+    assert lib.w4_chain_create(None, 1, WSP, 1 << 20, ctypes.byref(h)) == NULL
+    assert lib.w4_chain_create((w4.GemvDesc * 1)(desc()), 0, WSP, 1 << 20, ctypes.byref(h)) == ARG
+    assert lib.w4_chain_run(None, None) == ARG
+    lib.w4_chain_destroy(None)

@@ -320,3 +320,112 @@ def test_moe_small_shapes_and_determinism():
         for e in range(E):
             check_outputs(host.bf16_values(y1)[e], y_ref[e], xnorm(x[e]), np.abs(W[ids[e]]).max(axis=1),
                           f"moe E={E} K={K} N={N} slot {e}")
+
+
+# ------------------------------------------------------ persistent decode chain
+def _decode_linears(with_stage=True):
+    from gemm_w4_gemv_amd.decode import LAYER_STAGE
+    lins, host_in, specs = [], [], si.decode_step_specs()
+    for layer, idx, name, K, N in specs:
+        lin_np, x_bits = si.decode_linear(layer, idx)
+        t = host.int4_tensors(lin_np)
+        t["x"] = host.bf16_tensor(x_bits)
+        t["y"] = torch.zeros(N, dtype=torch.bfloat16, device=DEV)
+        t["stage"] = 4 * layer + LAYER_STAGE[name]
+        lins.append(t)
+        host_in.append((lin_np, x_bits))
+    return specs, lins, host_in
+
+
+def test_chain_decode_step_full_size():
+    """The 336-GEMV decode step as one persistent chain launch inside a graph (as the bench times it)."""
+    specs, lins, host_in = _decode_linears()
+    step = DecodeStep(lins, mode="chain")
+    torch.cuda.synchronize()
+    step.run_eager()
+    step.stream.synchronize()
+    assert step.chain.error() == 0
+    eager = [t["y"].clone() for t in lins]
+    step.capture()
+    for rep in range(3):
+        for t in lins:
+            t["y"].zero_()
+        torch.cuda.synchronize()
+        step.replay()
+        step.stream.synchronize()
+        for t, e in zip(lins, eager):
+            assert torch.equal(t["y"].view(torch.int16), e.view(torch.int16)), f"replay {rep} differs"
+    assert step.chain.error() == 0
+    g = si.rng(7, 0)
+    for (layer, idx, name, K, N), (lin_np, x_bits), t in zip(specs, host_in, lins):
+        rows = np.unique(np.concatenate([[0, N - 1], g.choice(N, 24, replace=False)]))
+        y = host.bf16_values(t["y"])[rows]
+        y_ref, wmax = int4_ref(lin_np, x_bits, rows)
+        check_outputs(y, y_ref[0], xnorm(x_bits), wmax, f"chain layer {layer} {name}")
+    step.destroy()
+
+
+def test_chain_data_dependent():
+    """Each stage reads the previous stage's output: q -> o -> gate -> down -> q -> o.
+
+    Outputs are zeroed before every run, so a stage that read its input
+    before the previous stage finished writing it would see zeros.  The
+    oracle runs the same chain, rounding each intermediate to BF16 as the
+    chain stores it.
+    """
+    shapes = [(3840, 4096), (4096, 3840), (3840, 15360), (15360, 3840), (3840, 4096), (4096, 3840)]
+    x0_bits = si.bf16_normal(8, (0,), (3840,))
+    gemvs, lin_nps = [], []
+    x_dev = host.bf16_tensor(x0_bits)
+    for i, (K, N) in enumerate(shapes):
+        lin_np = si.int4_linear(8, (1, i), K, N)
+        t = host.int4_tensors(lin_np)
+        t["x"] = x_dev
+        t["y"] = torch.zeros(N, dtype=torch.bfloat16, device=DEV)
+        t["stage"] = i
+        x_dev = t["y"]
+        gemvs.append(t)
+        lin_nps.append(lin_np)
+    # oracle chain
+    refs, x_bits = [], x0_bits
+    for lin_np in lin_nps:
+        y_ref, wmax = int4_ref(lin_np, x_bits)
+        refs.append((y_ref[0], wmax, xnorm(x_bits)))
+        x_bits = oracle.bf16_bits(y_ref[0])
+    step = DecodeStep(gemvs, mode="chain")
+    step.capture()
+    for rep in range(4):
+        for t in gemvs:
+            t["y"].zero_()
+        torch.cuda.synchronize()
+        step.replay()
+        step.stream.synchronize()
+        for i, (t, (y_ref, wmax, xn)) in enumerate(zip(gemvs, refs)):
+            check_outputs(host.bf16_values(t["y"]), y_ref, xn, wmax, f"dependent stage {i} replay {rep}")
+    assert step.chain.error() == 0
+    step.destroy()
+
+
+def test_chain_mixed_shapes():
+    """Stages mixing K classes (one, two and four waves per row), ragged N and tiny stages."""
+    plan = [[(128, 1), (1024, 7)], [(8192, 100)], [(4096, 1000), (15360, 3), (256, 33)], [(16384, 9)],
+            [(3840, 2)], [(512, 4096), (2048, 77)]]
+    gemvs, refs = [], []
+    for st, group in enumerate(plan):
+        for j, (K, N) in enumerate(group):
+            lin_np, x_bits = si.single_gemv(K, N, seed=40 + st * 8 + j)
+            t = host.int4_tensors(lin_np)
+            t["x"] = host.bf16_tensor(x_bits)
+            t["y"] = torch.zeros(N, dtype=torch.bfloat16, device=DEV)
+            t["stage"] = st * 3  # stage numbers need not be consecutive
+            gemvs.append(t)
+            y_ref, wmax = int4_ref(lin_np, x_bits)
+            refs.append((y_ref[0], wmax, xnorm(x_bits), f"stage {st} K={K} N={N}"))
+    step = DecodeStep(gemvs, mode="chain")
+    for rep in range(2):
+        step.run_eager()
+        step.stream.synchronize()
+        for t, (y_ref, wmax, xn, what) in zip(gemvs, refs):
+            check_outputs(host.bf16_values(t["y"]), y_ref, xn, wmax, what)
+    assert step.chain.error() == 0
+    step.destroy()
