@@ -12,53 +12,55 @@
 // 张量核心加速" (its last paragraph).
 //
 // The chain is a list of stages.  GEMVs of one stage are independent (q, k, v;
-// gate, up); a GEMV of stage s may read what stages < s wrote.  One 512-thread
-// workgroup runs per compute unit, its waves in two roles:
+// gate, up); a GEMV of stage s may read what stages < s wrote.  One
+// 1024-thread workgroup runs per compute unit, its 16 waves in three roles:
 //
-//  * Seven compute waves.  The rows of each stage are split evenly over all
-//    compute waves of the GPU.  A wave streams its rows as tiles of 8 chunk
-//    slots per lane (4 rows of K <= 4096, 2 of K <= 8192, 1 of K <= 16384)
-//    through three register sets, so up to three tiles are loading while one
-//    is computed -- across stage boundaries too: weights do not depend on
-//    earlier stages, so HBM keeps streaming while a stage barrier completes.
-//    x comes from LDS.  Outputs are stored with device-coherent (sc1,
-//    write-through) stores.  A wave issues its prefetches after a tile's
-//    stores, so at its last tile of a stage it can wait for exactly its
-//    stores (vmcnt(loads issued since)) before reporting the stage in LDS.
-//    Scale and zero of a slot-row arrive in one load (lanes 0-31 read the
-//    scales, 32-63 the zeros of the segment's 32 groups) and are shuffled
-//    to the lanes that use them: 12 memory instructions per 8 KB tile.
-//  * One control wave.  It stages each stage's x vectors into one of two
-//    LDS buffers, converted once into the dot2 pair layout.  An input that
-//    no earlier stage writes is staged through the caches while the previous
-//    stage still runs; an input written by an earlier stage is staged after
-//    that stage's barrier with device-coherent loads.  It waits until its
-//    compute waves have reported a stage, then announces the workgroup's
-//    progress on its own 128-byte flag line.  The control wave of workgroup
-//    0 also coordinates: it waits for every workgroup's flag and publishes
-//    the stage count on 64 "go" lines, each polled by a few control waves.
-//    All flag accesses are relaxed device-scope atomics; no L2 write-back
-//    or invalidate is ever issued (about 2 us per stage barrier on MI355X,
-//    against 15-90 us for a counter or fence based grid barrier).
+//  * kChainComputeWaves compute waves.  The tiles of each stage are split
+//    evenly over all compute waves of the GPU.  A tile is kChainTileRows
+//    slot-rows of 2 chunks (16 bytes of codes) per lane; x comes from LDS.
+//    A wave keeps one tile in flight: it computes a tile, stores its rows
+//    with device-coherent (sc1, write-through) stores, and only then issues
+//    the next tile's loads, so at its last tile of a stage vmcnt(loads just
+//    issued) proves its stores complete while the next stage's weights are
+//    already loading across the stage barrier.  A tile two or more stages
+//    ahead waits until the stage before it is released, so weights reach
+//    HBM in stage order.  Memory parallelism comes from the number of waves
+//    (a deeper per-wave ring makes the compiler's wait counts conservative
+//    at the loop head, and a deeper queue delays the barrier's own loads).
+//    Each wave publishes how many stages it has finished in an LDS word.
+//  * One control wave.  Once every compute wave of its workgroup has
+//    finished stage s, it announces that on its own 128-byte flag line.  The
+//    control wave of workgroup 0 also coordinates: it waits for every
+//    workgroup's flag and publishes the stage count on 64 "go" lines, each
+//    polled by a few control waves.  All flag accesses are relaxed
+//    device-scope atomics; no L2 write-back or invalidate is ever issued
+//    (about 2 us per stage barrier on MI355X, against 15-90 us for a counter
+//    or fence based grid barrier).
+//  * Staging waves (the rest, with the control wave among them).  After the
+//    barrier they stage the next stage's x vectors into one of two LDS
+//    buffers, converted once into the dot2 pair layout, splitting the 64-
+//    chunk slots between them so that the x of a stage arrives in one round
+//    trip.  Inputs written by an earlier stage are read with device-coherent
+//    loads.
 //
-// Compute waves never wait on another wave's memory counter, and the control
-// wave never waits on a weight load.  Every wait is bounded: past the spin
-// limit the waiter records an error in the workspace and leaves, so the
-// launch always ends.
+// Every wait is bounded: past the spin limit the waiter records an error in
+// the workspace and leaves (or, for a compute wave, goes on without waiting),
+// so the launch always ends.
 #include "chain.hpp"
 #include "gemv_common.hpp"
 
 namespace w4 {
 namespace {
 
-// Tile shape.  A tile is 4 slot-rows x 2 chunks per lane.  A row of C <= 128
-// chunks fills one slot-row (4 rows per tile); a longer row is cut into
-// sp = 2 or 4 segments of 128 chunks on consecutive slot-rows (2 or 1 rows
-// per tile), whose partial sums are added after the cross-lane reduction.
+// Tile shape.  A tile is kSlotRows slot-rows x 2 chunks per lane.  A row of
+// C <= 128 chunks fills one slot-row; a longer row is cut into sp = 2 or 4
+// segments of 128 chunks on consecutive slot-rows, whose partial sums are
+// added after the cross-lane reduction.
 // Slot-row q holds segment (q % sp) of row (q / sp); lane l's chunks in it
 // are 128 (q % sp) + l and + l + 64, in groups 32 (q % sp) + (l + 64 i) / 4.
-constexpr int kSlotRows = 4;
-constexpr int kTileLoads = 3 * kSlotRows;  // 8 weight loads + 4 scale/zero loads per tile
+constexpr int kSlotRows = kChainTileRows;
+constexpr int kSlotLanes = kWave / kSlotRows;  // lanes per slot-row after the row reduction
+constexpr int kTileLoads = 3 * kSlotRows;     // weight loads (2 per slot-row) and scale/zero loads (1)
 
 struct TileRegs {
     u32x4_t w[2 * kSlotRows];  // slot (q, i) in w[2 q + i]
@@ -78,11 +80,18 @@ struct Shared {
     // reports several at once, and a sum would then run ahead of waves still
     // working on an earlier stage.
     unsigned progress[kChainComputeWaves];
+    unsigned stage_go;  // stages whose x may be staged (inputs written, buffer free)
+    unsigned staged;    // shares of x staging finished, over all staging waves
     unsigned abort;
     unsigned base;
 };
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// s_waitcnt immediate that waits for vmcnt <= n only (expcnt and lgkmcnt at
+// their maxima): vmcnt bits 3:0 and 15:14.
+constexpr unsigned vmcnt_imm(unsigned n) { return (n & 15u) | 0x70u | 0xF00u | ((n >> 4) << 14); }
+static_assert(vmcnt_imm(0) == 0xF70u && vmcnt_imm(12) == 0xF7Cu && vmcnt_imm(24) == 0x4F78u, "vmcnt encoding");
 __device__ __forceinline__ int seg_shift(int sp) { return sp == 1 ? 0 : (sp == 2 ? 1 : 2); }
 
 __device__ __forceinline__ unsigned lds_load(const unsigned* p) {
@@ -141,7 +150,7 @@ __device__ __forceinline__ Work advance(const ChainLaunch& L, Work w, int v, int
     return first_from(L, w.s + 1, v, W);
 }
 
-// Issue the kTileLoads loads of one tile (no wait).  A dummy issue (past a
+// Issue the loads of one tile: 8 weight loads and 4 scale/zero loads (no wait).  A dummy issue (past a
 // wave's last tile) repeats w's scale/zero loads and gives its weight loads
 // an empty buffer range, which returns zeros without touching memory: the
 // same loads are issued on every path, so the compiler's wait counts for the
@@ -151,18 +160,10 @@ __device__ __forceinline__ void issue(const ChainLaunch& L, const Work& w, bool 
     const int C = G.C, N = G.N, Gr = C >> 2, sp = G.sp, sh = seg_shift(sp);
     const uint32_t row_bytes = (uint32_t)C * 16u;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(G.qw, dummy ? 0u : (uint32_t)N * row_bytes);
-#pragma unroll
-    for (int q = 0; q < kSlotRows; ++q) {
-        const uint32_t row = (uint32_t)(w.row + min(q >> sh, w.nrows - 1));
-        const int base = 128 * (q & (sp - 1));
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint32_t c = (uint32_t)min(base + lane + kWave * i, C - 1);
-            R.w[2 * q + i] = buf_load_b128<kAuxNontemporal>(rw, c * 16u, row * row_bytes);
-        }
-    }
-    // A global (not flat) pointer: flat loads would also count in lgkmcnt and
-    // make every LDS wait wait for the prefetches too.
+    // Issue order = use order (scales and zeros, then chunk column 0 of every
+    // slot-row, then column 1), so the math can start on the first arrivals.
+    // A global (not flat) pointer for the scales and zeros: flat loads would
+    // also count in lgkmcnt and make every LDS wait wait for the prefetches.
     typedef __attribute__((address_space(1))) const uint16_t g_u16;
     g_u16* sz = (g_u16*)(lane < 32 ? G.s : G.z);
 #pragma unroll
@@ -170,6 +171,15 @@ __device__ __forceinline__ void issue(const ChainLaunch& L, const Work& w, bool 
         const int row = w.row + min(q >> sh, w.nrows - 1);
         const int grp = min(32 * (q & (sp - 1)) + (lane & 31), Gr - 1);
         R.sz[q] = sz[(size_t)row * Gr + grp];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int q = 0; q < kSlotRows; ++q) {
+            const uint32_t row = (uint32_t)(w.row + min(q >> sh, w.nrows - 1));
+            const uint32_t c = (uint32_t)min(128 * (q & (sp - 1)) + lane + kWave * i, C - 1);
+            R.w[2 * q + i] = buf_load_b128<kAuxNontemporal>(rw, c * 16u, row * row_bytes);
+        }
     }
 }
 
@@ -224,18 +234,17 @@ __device__ __forceinline__ void compute(const ChainGemv& G, const Work& w, int l
             asm volatile("" : "+v"(acc[q])::"memory");
         }
     }
-    float total = reduce_rows<kSlotRows>(acc, lane);  // lane L: slot-row L / 16
-    if (sp >= 2) total += __shfl_xor(total, 16, kWave);
-    if (sp == 4) total += __shfl_xor(total, 32, kWave);
-    const int j = (lane >> 4) >> seg_shift(sp);  // row of the tile this lane's total belongs to
-    if ((lane & (16 * sp - 1)) == 0 && j < w.nrows) {
+    float total = reduce_rows<kSlotRows>(acc, lane);  // lane L: slot-row L / kSlotLanes
+    if (sp >= 2) total += __shfl_xor(total, kSlotLanes, kWave);
+    if (sp == 4) total += __shfl_xor(total, 2 * kSlotLanes, kWave);
+    const int j = (lane / kSlotLanes) >> seg_shift(sp);  // row of the tile this lane's total belongs to
+    if ((lane & (kSlotLanes * sp - 1)) == 0 && j < w.nrows) {
         const __amdgpu_buffer_rsrc_t ry = make_rsrc(G.y, (uint32_t)G.N * 2u);
         buf_store_u16_coherent(f32_to_bf16(total), ry, (uint32_t)(w.row + j) * 2u, 0);
     }
 }
 
 // --------------------------------------------------------------- control wave
-constexpr int kStageBatch = 4;  // slots of 64 x chunks loaded at once when staging x
 
 // Slot ``k`` of a stage's x staging: chunks [64 m, 64 m + 64) of GEMV g
 // (slots cover each GEMV's padded chunk count).
@@ -258,67 +267,91 @@ __device__ __forceinline__ int stage_slots(const ChainLaunch& L, const ChainStag
     return n;
 }
 
-// Staging of a stage's x into an LDS buffer, in batches of kStageBatch slots:
-// bf16 pairs in the dot2 order (word p of chunk c at 16 (p Cp + c)), then the
-// chunk sums; padding chunks are zeros.  issue() only loads (inputs written
-// by an earlier stage device-coherently), so the loads can be in flight while
-// the wave waits; finish() converts and writes.
-struct XBatch {
-    u32x4_t raw[kStageBatch][4];
-};
-
-__device__ __forceinline__ void stage_issue(const ChainLaunch& L, const ChainStage& st, int b0, int lane, XBatch& B) {
+// Staging of a stage's x into an LDS buffer: bf16 pairs in the dot2 order
+// (word p of chunk c at 16 (p Cp + c)), then the chunk sums; padding chunks
+// are zeros.  The staging waves split the stage's slots (slot k goes to
+// staging wave k mod kChainStagers), so a stage's x arrives in one round trip.
+__device__ __forceinline__ void stage_load(const ChainLaunch& L, int g, int m, int lane, u32x4_t raw[4]) {
+    const ChainGemv& G = L.gemvs[g];
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(G.x, (uint32_t)G.C * 64u);
+    const uint32_t c = (uint32_t)min(m * kWave + lane, G.C - 1);
+    if (G.x_internal) {  // written by an earlier stage: device-coherent loads
 #pragma unroll
-    for (int j = 0; j < kStageBatch; ++j) {
-        int g, m;
-        if (!stage_slot(L, st, b0 + j, g, m)) break;
-        const ChainGemv& G = L.gemvs[g];
-        const __amdgpu_buffer_rsrc_t rx = make_rsrc(G.x, (uint32_t)G.C * 64u);
-        const uint32_t c = (uint32_t)min(m * kWave + lane, G.C - 1);
-        if (G.x_internal) {
+        for (int p = 0; p < 4; ++p) raw[p] = buf_load_b128_coherent(rx, c * 64u + 16u * p, 0);
+    } else {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) B.raw[j][p] = buf_load_b128_coherent(rx, c * 64u + 16u * p, 0);
-        } else {
-#pragma unroll
-            for (int p = 0; p < 4; ++p) B.raw[j][p] = buf_load_b128<0>(rx, c * 64u + 16u * p, 0);
-        }
+        for (int p = 0; p < 4; ++p) raw[p] = buf_load_b128<0>(rx, c * 64u + 16u * p, 0);
     }
 }
 
-__device__ __forceinline__ void stage_finish(const ChainLaunch& L, const ChainStage& st, int b0, int lane,
-                                             const XBatch& B, unsigned char* xb) {
+__device__ __forceinline__ void stage_write(const ChainLaunch& L, int g, int m, int lane, const u32x4_t raw[4],
+                                            unsigned char* xb) {
+    const ChainGemv& G = L.gemvs[g];
+    const int C = G.C, Cp = chain_x_chunks(C), c = m * kWave + lane;
+    unsigned char* xg = xb + G.x_lds;
+    uint32_t xp[16];
+    float sum = 0.f;
+    if (c < C) {
+        sum = x_chunk_pairs(raw, xp);
+    } else {
 #pragma unroll
-    for (int j = 0; j < kStageBatch; ++j) {
-        int g, m;
-        if (!stage_slot(L, st, b0 + j, g, m)) break;
-        const ChainGemv& G = L.gemvs[g];
-        const int C = G.C, Cp = chain_x_chunks(C), c = m * kWave + lane;
-        unsigned char* xg = xb + G.x_lds;
-        uint32_t xp[16];
-        float sum = 0.f;
-        if (c < C) {
-            sum = x_chunk_pairs(B.raw[j], xp);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 16; ++k) xp[k] = 0u;
-        }
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-            *reinterpret_cast<u32x4_t*>(xg + ((size_t)p * Cp + c) * 16) =
-                u32x4_t{xp[4 * p], xp[4 * p + 1], xp[4 * p + 2], xp[4 * p + 3]};
-        *reinterpret_cast<float*>(xg + (size_t)64 * Cp + (size_t)c * 4) = sum;
+        for (int k = 0; k < 16; ++k) xp[k] = 0u;
     }
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        *reinterpret_cast<u32x4_t*>(xg + ((size_t)p * Cp + c) * 16) =
+            u32x4_t{xp[4 * p], xp[4 * p + 1], xp[4 * p + 2], xp[4 * p + 3]};
+    *reinterpret_cast<float*>(xg + (size_t)64 * Cp + (size_t)c * 4) = sum;
 }
 
-// Whole staging of stage s (all batches, loads then writes per batch).
-__device__ void stage_x(const ChainLaunch& L, int s, unsigned char* xb, int lane) {
+// This staging wave's share of stage s: slots sid, sid + S, ... (two at a time).
+__device__ void stage_share(const ChainLaunch& L, int s, unsigned char* xb, int lane, int sid) {
     const ChainStage st = L.stages[s];
     const int n = stage_slots(L, st);
-    for (int b0 = 0; b0 < n; b0 += kStageBatch) {
-        XBatch B;
-        stage_issue(L, st, b0, lane, B);
-        stage_finish(L, st, b0, lane, B, xb);
+    for (int k = sid; k < n; k += 2 * kChainStagers) {
+        int g0, m0, g1 = 0, m1 = 0;
+        stage_slot(L, st, k, g0, m0);
+        const bool two = stage_slot(L, st, k + kChainStagers, g1, m1);
+        u32x4_t r0[4], r1[4];
+        stage_load(L, g0, m0, lane, r0);
+        if (two) stage_load(L, g1, m1, lane, r1);
+        stage_write(L, g0, m0, lane, r0, xb);
+        if (two) stage_write(L, g1, m1, lane, r1, xb);
     }
+}
+
+// Staging wave sid (1 .. kChainStagers - 1; the control wave is staging wave
+// 0): stage 0 at once, stage t once the control wave has seen the barrier
+// after stage t - 1 (then stage t's inputs are written and the LDS buffer it
+// reuses is free); count each finished share in sh.staged.
+__device__ void staging_wave(const ChainLaunch& L, Shared& sh, unsigned char* xl, int lane, int sid) {
+    for (int t = 0; t < L.num_stages; ++t) {
+        if (t > 0) {
+            unsigned n = 0, r = lds_load(&sh.stage_go), ab = lds_load(&sh.abort);
+            while ((r < (unsigned)t) & (ab == 0u) & (n <= L.spin_limit)) {
+                __builtin_amdgcn_s_sleep(1);
+                ++n;
+                r = lds_load(&sh.stage_go);
+                ab = lds_load(&sh.abort);
+            }
+            if (r < (unsigned)t) return;  // aborted or timed out: the control wave reports it
+        }
+        stage_share(L, t, xl + (size_t)(t & 1) * kChainXLdsBytes, lane, sid);
+        if (lane == 0) __hip_atomic_fetch_add(&sh.staged, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+}
+
+// Wait until every staging wave has staged stage t, then release it to the
+// compute waves.
+__device__ __forceinline__ bool release_x(const ChainLaunch& L, Shared& sh, int t) {
+    const unsigned want = (unsigned)kChainStagers * ((unsigned)t + 1u);
+    unsigned n = 0;
+    while (lds_load(&sh.staged) < want) {
+        if (lds_load(&sh.abort) || ++n > L.spin_limit) { set_error(L, sh, 8u); return false; }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __hip_atomic_store(&sh.x_ready, (unsigned)t + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return true;
 }
 
 __device__ void control_wave(const ChainLaunch& L, Shared& sh, unsigned char* xl, int lane) {
@@ -326,18 +359,10 @@ __device__ void control_wave(const ChainLaunch& L, Shared& sh, unsigned char* xl
     unsigned* my_flag = L.flags + (size_t)wg * kChainLineWords;
     const unsigned* my_go = L.go + (size_t)(wg % kChainGoLines) * kChainLineWords;
     const unsigned base = sh.base;
-    stage_x(L, 0, xl, lane);
-    __hip_atomic_store(&sh.x_ready, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    stage_share(L, 0, xl, lane, 0);
+    if (lane == 0) __hip_atomic_fetch_add(&sh.staged, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (!release_x(L, sh, 0)) return;
     for (int s = 0; s < L.num_stages; ++s) {
-        const bool more = s + 1 < L.num_stages;
-        unsigned char* xnext = xl + (size_t)((s + 1) & 1) * kChainXLdsBytes;
-        // Inputs of the next stage that no stage writes are staged now, while
-        // the compute waves work on stage s: the buffer held stage s - 1's x,
-        // which this workgroup's compute waves are done with.  Only their
-        // release waits for the barrier.
-        const bool early = more && !L.stages[s + 1].x_internal;
-        if (early) stage_x(L, s + 1, xnext, lane);
-
         // Every compute wave of this workgroup has finished stage s (stores complete).
         unsigned n = 0;
         while (__builtin_amdgcn_ballot_w64(lane < kChainComputeWaves &&
@@ -348,7 +373,7 @@ __device__ void control_wave(const ChainLaunch& L, Shared& sh, unsigned char* xl
         }
         const unsigned target = base + (unsigned)s + 1u;
         if (lane == 0) flag_store(my_flag, target);
-        if (!more) break;  // nothing waits for the last stage
+        if (s + 1 >= L.num_stages) break;  // nothing waits for the last stage
 
         if (wg == 0) {  // coordinator: every workgroup's stage s, then publish
             for (int w = lane; w < P; w += kWave) {
@@ -366,8 +391,12 @@ __device__ void control_wave(const ChainLaunch& L, Shared& sh, unsigned char* xl
             if (++n > L.spin_limit) { set_error(L, sh, 2u); return; }
             __builtin_amdgcn_s_sleep(1);
         }
-        if (!early) stage_x(L, s + 1, xnext, lane);
-        __hip_atomic_store(&sh.x_ready, (unsigned)s + 2u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        // Stage s + 1 may be staged: its inputs are written, and its LDS
+        // buffer (stage s - 1's) is free.
+        __hip_atomic_store(&sh.stage_go, (unsigned)s + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        stage_share(L, s + 1, xl + (size_t)((s + 1) & 1) * kChainXLdsBytes, lane, 0);
+        if (lane == 0) __hip_atomic_fetch_add(&sh.staged, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (!release_x(L, sh, s + 1)) return;
     }
 }
 
@@ -398,38 +427,48 @@ __device__ void compute_wave(const ChainLaunch& L, Shared& sh, const unsigned ch
     report(a.s);  // no tiles in the first a.s stages; nothing pending
     int x_stage = -1;  // stage whose x this workgroup has staged and released
 
-    // Compute the tile w (its loads in R); then, if nxt is in a later stage,
-    // wait for the stores and report w's stage done.
-    auto run = [&](const Work& w, const TileRegs& R, const Work& nxt) {
-        if (x_stage != w.s) {
-            wait_x(w.s);
-            x_stage = w.s;
-        }
-        const ChainGemv G = L.gemvs[w.g];
-        compute(G, w, lane, R, xl + (size_t)(w.s & 1) * kChainXLdsBytes + G.x_lds);
-        if (nxt.s != w.s) {
-            __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's stores are complete
-            report(nxt.s);
-        }
-    };
+    if (a.s >= L.num_stages) return;
 
-    // Two tiles per iteration, both loaded before either is computed (and
-    // before any wait for x, so the loads overlap the stage barrier).  Nothing
-    // stays in flight from one iteration to the next, so the compiler's own
-    // wait counts are exact; latency is hidden by the other compute waves.
-    // Past the last tile the second issue is a dummy (empty buffer range).
-    while (a.s < L.num_stages) {
+    // One tile in flight per wave: compute it, store its rows, then issue the
+    // next tile's loads.  The stores go out before those loads, so at the end
+    // of a stage vmcnt(kTileLoads) (the loads just issued) proves them
+    // complete while the next stage's weights are already on their way across
+    // the stage barrier.  A tile two or more stages ahead is not issued until
+    // the stage before it is released: weights then reach the memory system
+    // in stage order, and a stage's tiles do not queue behind later stages'.
+    // Nothing but the tile in R is in flight at the loop head, so the
+    // compiler's waits there are exact.
+    TileRegs R;
+    issue(L, a, false, lane, R);
+    for (;;) {
+        if (x_stage != a.s) {
+            wait_x(a.s);
+            x_stage = a.s;
+        }
+        const ChainGemv G = L.gemvs[a.g];
+        compute(G, a, lane, R, xl + (size_t)(a.s & 1) * kChainXLdsBytes + G.x_lds);
+        // Keep the next tile's loads below this tile's stores.
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
         const Work b = advance(L, a, v, W);
         const bool has_b = b.s < L.num_stages;
-        TileRegs RA, RB;
-        issue(L, a, false, lane, RA);
-        issue(L, has_b ? b : a, !has_b, lane, RB);
-        run(a, RA, b);
+        const bool near = has_b && b.s <= a.s + 1;
+        if (near) issue(L, b, false, lane, R);
+        if (b.s != a.s) {
+            if (near)
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTileLoads));  // only the loads just issued may be pending
+            else
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            report(b.s);
+        }
         if (!has_b) break;
-        const Work c = advance(L, b, v, W);
-        run(b, RB, c);
-        a = c;
+        if (!near) {
+            wait_x(b.s - 1);
+            issue(L, b, false, lane, R);
+        }
+        a = b;
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainStage* __restrict__ stages,
@@ -447,15 +486,19 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainStage* 
     if (tid == 0) {
         sh.x_ready = 0;
         for (int i = 0; i < kChainComputeWaves; ++i) sh.progress[i] = 0;
+        sh.stage_go = 0;
+        sh.staged = 0;
         sh.abort = 0;
         sh.base = flag_load(L.flags + (size_t)blockIdx.x * kChainLineWords);
     }
     __syncthreads();  // the only workgroup barrier: roles split below
     if (wave == 0) {
         control_wave(L, sh, xl, lane);
-    } else {
+    } else if (wave <= kChainComputeWaves) {
         const int W = L.workers * kChainComputeWaves;
         compute_wave(L, sh, xl, lane, wave - 1, uniform((int)blockIdx.x * kChainComputeWaves + (wave - 1)), W);
+    } else {
+        staging_wave(L, sh, xl, lane, wave - kChainComputeWaves);
     }
 }
 

@@ -18,7 +18,7 @@ struct ChainGemv {
     int C;           // K / 32 chunks of 16 bytes per row
     int N;
     int sp;          // segments of 128 chunks per row: 1 (K <= 4096), 2 (K <= 8192) or 4 (K <= 16384)
-    int tile0;       // first tile of this GEMV in its stage (tiles are 4 / sp rows)
+    int tile0;       // first tile of this GEMV in its stage (tiles are kChainTileRows / sp rows)
     int x_lds;       // byte offset of this GEMV's staged x in its LDS buffer
     int x_internal;  // 1: x is written by an earlier stage of the chain
 };
@@ -32,14 +32,15 @@ struct ChainStage {
     int x_internal;  // 1: some input of the stage is written by an earlier stage
 };
 
-constexpr int kChainThreads = 1024;  // 16 waves: 1 control + 15 compute
-constexpr int kChainComputeWaves = 15;
+constexpr int kChainThreads = 1024;  // 16 waves: 1 control, kChainComputeWaves compute, the rest staging
+constexpr int kChainComputeWaves = 8;
+constexpr int kChainStagers = 16 - kChainComputeWaves;  // staging waves, the control wave included
 constexpr int kChainMaxWorkers = 1024;
 constexpr int kChainGoLines = 64;
+constexpr int kChainTileRows = 4;     // slot-rows per compute-wave tile: 4 / sp rows of a GEMV
 constexpr int kChainLineWords = 32;    // one 128-byte line per flag
 constexpr int kChainMaxC = 512;        // K <= 16384
 constexpr int kChainXLdsBytes = 65536; // staged x (pairs + chunk sums) of one stage; two buffers
-constexpr int kChainSlots = 8;         // chunk slots per lane per tile
 
 // Staged x of one GEMV is zero-padded to whole segments of 128 chunks, so
 // the kernel never masks a chunk index.

@@ -287,7 +287,7 @@ W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* wor
         if (x_bytes > w4::kChainXLdsBytes)
             return fail(W4_ERR_SHAPE, "%s: the inputs of stage %d need %d bytes of LDS (limit %d)",
                         fn, d.stage, x_bytes, w4::kChainXLdsBytes);
-        const int rows_per_tile = 4 / g.sp;
+        const int rows_per_tile = w4::kChainTileRows / g.sp;
         st.tiles += (d.N + rows_per_tile - 1) / rows_per_tile;
         st.ngemv += 1;
     }
