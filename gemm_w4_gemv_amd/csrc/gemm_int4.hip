@@ -8,17 +8,26 @@
 // quantisation group) unpacks a 64 x 128 weight tile, computes
 // bf16((q - z) * s) with round-to-nearest-even, stores it in LDS, and the
 // eight waves of the workgroup feed it to v_mfma_f32_16x16x32_bf16 as the B
-// operand.  The activation fragments (A operand) are read straight from
-// device memory in the MFMA lane layout (8 consecutive k per lane), so they
-// need no LDS.
+// operand.  The activation tile (A operand, 128 x 128 per K-step) is loaded
+// once per workgroup with full-line loads and staged in LDS beside it.
 //
 // Tile: 128 (M) x 64 (N) per workgroup; wave w computes rows 32 (w % 4) ..
 // +32 and columns 32 (w / 4) .. +32 as 2 x 2 MFMA blocks of 16 x 16.  The
-// weight tile is double-buffered in LDS so the next tile's global loads and
-// dequantisation overlap the current tile's MFMAs, with one barrier per
-// K-step.  When the N x M tiles cannot fill the GPU, K is split; each split
-// writes FP32 partials to the caller's workspace and a second kernel adds
-// them in split order (deterministic, no atomics).
+// activation and dequantised weight tiles are double-buffered in LDS, with
+// one barrier per K-step of 128.  Global loads run kDepth K-steps ahead of
+// the MFMAs: this thread's 64 bytes of the next kDepth activation tiles and
+// its packed weights, scales and zeros of the next kDepth weight tiles live
+// in a ring of registers, the loop unrolled kDepth times so every ring slot
+// is a fixed register set (up to kDepth - 1 surplus steps at the end compute
+// on zeros: loads past the K range use an empty buffer range, which returns
+// zeros without touching memory).  The staging of step j + 1 (dequantise,
+// LDS stores) is spread between step j's MFMAs.  LDS traffic (fragment reads
+// and staging stores, 176 KB per K-step) is what bounds this kernel on
+// MI355X; MFMA issue and global loads are not (removing either leaves the
+// time unchanged).  All loads are buffer loads (weights non-temporal).  When
+// the N x M tiles cannot fill the GPU, K is split; each split writes FP32
+// partials to the caller's workspace and a second kernel adds them in split
+// order (deterministic, no atomics).
 #include "w4_device.hpp"
 #include "w4_internal.hpp"
 
@@ -27,20 +36,35 @@ namespace {
 
 constexpr int kBM = 128, kBN = 64, kBK = 128;
 constexpr int kThreads = 512;
-constexpr int kLdsStride = kBK + 8;  // bf16 elements per LDS row; +16 bytes keeps ds_read_b128 conflict-free
+constexpr int kDepth = 2;            // K-steps of loads in flight ahead of the MFMAs
 constexpr int kTargetBlocks = 256;   // one workgroup per compute unit of an MI355X
+
+// LDS tiles are rows of kBK bf16 (16 chunks of 16 bytes), chunk c of row r
+// stored at chunk position c ^ (r % 16): the 16 rows an MFMA fragment read
+// touches at one chunk, and the 16 chunks of one row a staging write
+// touches, each land on 16 distinct positions, i.e. on all 64 banks once.
+__device__ __forceinline__ int lds_elem(int row, int chunk) { return row * kBK + ((chunk ^ (row & 15)) << 3); }
 
 __device__ __forceinline__ void mfma_16x16x32(const u32x4_t& a, const u32x4_t& b, f32x4_t& acc) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
 }
 
+// One ring slot: this thread's share of one K-step's activation tile (chunk
+// tid % 16 of rows tid / 16 + 32 i) and of its packed weight tile (16 codes
+// of one row, with that row's scale and zero).
+struct Slot {
+    u32x4_t a[4];
+    u32x4_t w;  // .x, .y: codes; .z, .w: scale and zero bits
+};
+
 template <bool kSplit>
 __global__ __launch_bounds__(kThreads) void gemm_int4_mfma_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ s,
     const uint16_t* __restrict__ z, uint16_t* __restrict__ y, float* __restrict__ ws, int M, int K,
     int N, int splits) {
-    __shared__ __attribute__((aligned(16))) uint16_t wt[2][kBN][kLdsStride];
+    __shared__ __attribute__((aligned(16))) uint16_t wt[2][kBN * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t at[2][kBM * kBK];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -52,61 +76,78 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_mfma_kernel(
     const int G = K / kBK;
     const int kt0 = (int)(((long)blockIdx.z * KT) / splits);
     const int kt1 = (int)(((long)(blockIdx.z + 1) * KT) / splits);
+    const int nsteps = kt1 - kt0;
     const int words_per_row = K / 8;
 
-    // Weight-tile loader: thread -> (row r, 16 codes at k = 16 part).
+    // Weight-tile loader: thread -> (row r, 16 codes at k = 16 part).  Rows
+    // past N read row N - 1 (never stored).
     const int lr = tid >> 3, part = tid & 7;
-    const bool row_ok = (n0 + lr) < N;
-    const uint32_t* wrow = qw + (size_t)(row_ok ? n0 + lr : 0) * words_per_row + 2 * part;
-    const uint16_t* srow = s + (size_t)(row_ok ? n0 + lr : 0) * G;
-    const uint16_t* zrow = z + (size_t)(row_ok ? n0 + lr : 0) * G;
+    const int wr = min(n0 + lr, N - 1);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qw, (uint32_t)((size_t)N * words_per_row * 4));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, (uint32_t)((size_t)N * G * 2));
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(z, (uint32_t)((size_t)N * G * 2));
+    const __amdgpu_buffer_rsrc_t rnone = make_rsrc(qw, 0u);
+    const uint32_t qoff = (uint32_t)(((size_t)wr * words_per_row + 2 * part) * 4);
+    const uint32_t szoff = (uint32_t)((size_t)wr * G * 2);
 
-    // Activation fragments: lane -> row (lane & 15) of each 16-row block, k = 8 (lane >> 4) + 0..7.
-    int arow[2];
+    // Activation tile loader: chunk tid % 16 of rows tid / 16 + 32 i: each
+    // load instruction covers 4 whole rows (8 whole 128-byte lines).  Rows
+    // past M read row M - 1; their results are never stored.
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)((size_t)M * K * 2));
+    const int ar = tid >> 4, ac = tid & 15;
+    uint32_t aoff[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int m = m0 + 32 * wm + 16 * i + (lane & 15);
-        arow[i] = m < M ? m : M - 1;  // rows past M read a valid row; their results are never stored
-    }
-    const int acol = 8 * (lane >> 4);
+    for (int i = 0; i < 4; ++i) aoff[i] = (uint32_t)(((size_t)min(m0 + ar + 32 * i, M - 1) * K + 8 * ac) * 2);
 
-    u32x2_t wreg;
-    float sreg, zreg;
-    auto load_w = [&](int kt) {
-        if (row_ok) {
-            wreg = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(wrow + kt * 16));
-            sreg = f16_to_f32(srow[kt]);
-            zreg = f16_to_f32(zrow[kt]);
+    // Loads of K-step kt0 + j into a slot (an empty range past the split's end).
+    auto issue = [&](int j, Slot& S) {
+        const bool live = j < nsteps;
+        const int kt = kt0 + (live ? j : 0);
+        const __amdgpu_buffer_rsrc_t ra = live ? rx : rnone;
+        const __amdgpu_buffer_rsrc_t rqq = live ? rq : rnone;
+        const __amdgpu_buffer_rsrc_t rss = live ? rs : rnone;
+        const __amdgpu_buffer_rsrc_t rzz = live ? rz : rnone;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S.a[i] = buf_load_b128(ra, aoff[i], (uint32_t)(kt * kBK) * 2u);
+        const u32x2_t q = __builtin_bit_cast(
+            u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rqq, (int)qoff, (int)sgpr((uint32_t)kt * 64u), kAuxNontemporal));
+        S.w.x = q.x;
+        S.w.y = q.y;
+        S.w.z = buf_load_u16(rss, szoff, (uint32_t)kt * 2u);
+        S.w.w = buf_load_u16(rzz, szoff, (uint32_t)kt * 2u);
+    };
+    // Staging of one K-step into LDS buffer ``buf``, in four parts that the
+    // main loop interleaves with its MFMAs: dequantise this thread's 16 codes
+    // (part 0) and store them (1), store its activations (2, 3).
+    u32x4_t wlo, whi;
+    auto stage = [&](const Slot& S, int buf, int part_no) {
+        if (part_no == 0) {
+            const float sc = f16_to_f32((uint16_t)S.w.z), zp = f16_to_f32((uint16_t)S.w.w);
+            float f[16];
+            int4_word_dequant_f32(S.w.x, sc, zp, f);
+            int4_word_dequant_f32(S.w.y, sc, zp, f + 8);
+            wlo.x = pack_bf16x2(f[0], f[1]);
+            wlo.y = pack_bf16x2(f[2], f[3]);
+            wlo.z = pack_bf16x2(f[4], f[5]);
+            wlo.w = pack_bf16x2(f[6], f[7]);
+            whi.x = pack_bf16x2(f[8], f[9]);
+            whi.y = pack_bf16x2(f[10], f[11]);
+            whi.z = pack_bf16x2(f[12], f[13]);
+            whi.w = pack_bf16x2(f[14], f[15]);
+        } else if (part_no == 1) {
+            *reinterpret_cast<u32x4_t*>(&wt[buf][lds_elem(lr, 2 * part)]) = wlo;
+            *reinterpret_cast<u32x4_t*>(&wt[buf][lds_elem(lr, 2 * part + 1)]) = whi;
         } else {
-            wreg = u32x2_t{0u, 0u};
-            sreg = 0.f;
-            zreg = 0.f;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int i = 2 * (part_no - 2) + h;
+                *reinterpret_cast<u32x4_t*>(&at[buf][lds_elem(ar + 32 * i, ac)]) = S.a[i];
+            }
         }
     };
-    auto store_w = [&](int buf) {
-        float f[16];
-        int4_word_dequant_f32(wreg.x, sreg, zreg, f);
-        int4_word_dequant_f32(wreg.y, sreg, zreg, f + 8);
-        u32x4_t lo, hi;
-        lo.x = pack_bf16x2(f[0], f[1]);
-        lo.y = pack_bf16x2(f[2], f[3]);
-        lo.z = pack_bf16x2(f[4], f[5]);
-        lo.w = pack_bf16x2(f[6], f[7]);
-        hi.x = pack_bf16x2(f[8], f[9]);
-        hi.y = pack_bf16x2(f[10], f[11]);
-        hi.z = pack_bf16x2(f[12], f[13]);
-        hi.w = pack_bf16x2(f[14], f[15]);
-        u32x4_t* dst = reinterpret_cast<u32x4_t*>(&wt[buf][lr][16 * part]);
-        dst[0] = lo;
-        dst[1] = hi;
-    };
-    u32x4_t a[2][4];
-    auto load_a = [&](int kt, u32x4_t (&dst)[2][4]) {
+    auto store_w = [&](const Slot& S, int buf) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                dst[i][ks] = *reinterpret_cast<const u32x4_t*>(x + (size_t)arow[i] * K + kt * kBK + 32 * ks + acol);
+        for (int p = 0; p < 4; ++p) stage(S, buf, p);
     };
 
     f32x4_t acc[2][2];
@@ -115,38 +156,48 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_mfma_kernel(
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    if (kt0 < kt1) {
-        load_w(kt0);
-        load_a(kt0, a);
-        store_w(0);
+    // Step j (0-based within the split) computes from LDS buffer j & 1; before
+    // its barrier it stages step j + 1 (slot (j + 1) % kDepth) into the other
+    // buffer, then refills slot j % kDepth with step j + kDepth.
+    Slot ring[kDepth];
+    if (nsteps > 0) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) issue(d, ring[d]);
+        store_w(ring[0], 0);
         __syncthreads();
-        for (int kt = kt0; kt < kt1; ++kt) {
-            const int buf = (kt - kt0) & 1;
-            const bool more = kt + 1 < kt1;
-            u32x4_t an[2][4];
-            if (more) {
-                load_w(kt + 1);
-                load_a(kt + 1, an);
+        for (int j0 = 0; j0 < nsteps; j0 += kDepth) {
+#pragma unroll
+            for (int d = 0; d < kDepth; ++d) {
+                const int j = j0 + d;
+                const int buf = j & 1;
+                Slot& S = ring[d];
+                const Slot& T = ring[(d + 1) % kDepth];
+                // All fragments of the step first, so the LDS reads overlap
+                // each other rather than each waiting before its MFMAs.
+                u32x4_t a[4][2], b[4][2];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        a[ks][i] = *reinterpret_cast<const u32x4_t*>(
+                            &at[buf][lds_elem(32 * wm + 16 * i + (lane & 15), 4 * ks + (lane >> 4))]);
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj)
+                        b[ks][jj] = *reinterpret_cast<const u32x4_t*>(
+                            &wt[buf][lds_elem(32 * wn + 16 * jj + (lane & 15), 4 * ks + (lane >> 4))]);
+                }
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int jj = 0; jj < 2; ++jj) mfma_16x16x32(a[ks][i], b[ks][jj], acc[i][jj]);
+                    // Part ks of step j + 1's staging runs while these MFMAs execute.
+                    stage(T, buf ^ 1, ks);
+                }
+                issue(j + kDepth, S);
+                __syncthreads();
             }
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                u32x4_t b[2];
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    b[j] = *reinterpret_cast<const u32x4_t*>(&wt[buf][32 * wn + 16 * j + (lane & 15)][32 * ks + acol]);
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) mfma_16x16x32(a[i][ks], b[j], acc[i][j]);
-            }
-            if (more) {
-                store_w(buf ^ 1);
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) a[i][ks] = an[i][ks];
-            }
-            __syncthreads();
         }
     }
 
@@ -154,17 +205,17 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int n = n0 + 32 * wn + 16 * j + (lane & 15);
+        for (int jj = 0; jj < 2; ++jj) {
+            const int n = n0 + 32 * wn + 16 * jj + (lane & 15);
             if (n >= N) continue;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int m = m0 + 32 * wm + 16 * i + 4 * (lane >> 4) + e;
                 if (m >= M) continue;
                 if constexpr (kSplit) {
-                    ws[((size_t)blockIdx.z * M + m) * N + n] = acc[i][j][e];
+                    ws[((size_t)blockIdx.z * M + m) * N + n] = acc[i][jj][e];
                 } else {
-                    y[(size_t)m * N + n] = f32_to_bf16(acc[i][j][e]);
+                    y[(size_t)m * N + n] = f32_to_bf16(acc[i][jj][e]);
                 }
             }
         }
