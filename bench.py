@@ -24,6 +24,16 @@ Also reported, outside the timed step:
     same step.
 
     python bench.py [--steps K] [--warmup W] [--no-extra] [--no-cpu-baseline]
+    python bench.py --counters   # only the kernels that HBM counters are read for
+
+``--counters`` runs five chain-kernel launches of the decode step, then five
+copies of 512 MiB by torch (a plain copy of known size, read once and
+written once), for ``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE``
+runs.  The counters' per-launch figures for the chain kernel, scaled by
+what the same counters read for the copy, give ``roofline.traffic``; the
+result is kept in profiles/chain_kernel_traffic.json together with a hash
+of the chain kernel's sources, and ``traffic`` is reported only while that
+hash still matches.
 """
 from __future__ import annotations
 
@@ -52,7 +62,35 @@ def parse():
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the FP64 oracle")
     p.add_argument("--cpu-layers", type=int, default=1, help="decode layers the oracle sample covers")
+    p.add_argument("--counters", action="store_true",
+                   help="run only five chain launches and five 512 MiB copies (for HBM counter runs)")
     return p.parse_args()
+
+
+# Sources that define the chain kernel; a traffic figure measured on other
+# sources is not reported.
+CHAIN_SOURCES = ["gemm_w4_gemv_amd/csrc/chain.hip", "gemm_w4_gemv_amd/csrc/chain.hpp",
+                 "gemm_w4_gemv_amd/csrc/gemv_common.hpp", "gemm_w4_gemv_amd/csrc/w4_device.hpp"]
+TRAFFIC_FILE = ROOT / "profiles" / "chain_kernel_traffic.json"
+
+
+def chain_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in CHAIN_SOURCES:
+        h.update((ROOT / rel).read_bytes())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per chain launch from the committed counter runs, if they match the current sources."""
+    try:
+        rec = json.loads(TRAFFIC_FILE.read_text())
+    except (OSError, ValueError):
+        return None
+    if rec.get("chain_source_sha256") != chain_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 # ------------------------------------------------------------------ helpers
@@ -224,6 +262,29 @@ def cpu_baseline(si, rf, layers: int):
 
 
 # --------------------------------------------------------------------- main
+def counter_run(torch, host, si) -> int:
+    """Five chain launches of the decode step, then five 512 MiB torch copies."""
+    from gemm_w4_gemv_amd.decode import DecodeStep
+    lins = decode_linears(host, si, torch)
+    step = DecodeStep(lins, mode="chain")
+    torch.cuda.synchronize()
+    for _ in range(5):
+        step.run_eager()
+    step.stream.synchronize()
+    err = step.chain.error()
+    step.destroy()
+    del lins
+    src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"counters run: 5 chain launches (error word {err:#x}), 5 copies of {src.numel()} bytes")
+    return 1 if err else 0
+
+
 def main() -> int:
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -247,6 +308,9 @@ def main() -> int:
         return 1
 
     from gemm_w4_gemv_amd.decode import DecodeStep
+
+    if args.counters:
+        return counter_run(torch, host, si)
 
     log("generating and uploading the decode step (336 INT4 linears)")
     lins = decode_linears(host, si, torch)
@@ -291,7 +355,7 @@ def main() -> int:
     avg_us = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / reps
     achieved = step_bytes / (avg_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / rf.HBM_PEAK_GBPS, 4), "traffic": None,
+                "frac": round(achieved / rf.HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
                 "kernel": "chain_kernel (336 INT4 GEMVs, 192 stages, one launch per decode step)",
                 "bytes_per_launch": step_bytes, "avg_launch_us": round(avg_us, 2), "launches_timed": reps}
     log(f"chain kernel: {avg_us:.1f} us/launch, {achieved:.0f} GB/s")
