@@ -36,12 +36,13 @@
 //    device-scope atomics; no L2 write-back or invalidate is ever issued
 //    (about 2 us per stage barrier on MI355X, against 15-90 us for a counter
 //    or fence based grid barrier).
-//  * Staging waves (the rest, with the control wave among them).  After the
-//    barrier they stage the next stage's x vectors into one of two LDS
-//    buffers, converted once into the dot2 pair layout, splitting the 64-
-//    chunk slots between them so that the x of a stage arrives in one round
-//    trip.  Inputs written by an earlier stage are read with device-coherent
-//    loads.
+//  * Staging waves (the rest).  They stage each stage's x vectors into one
+//    of two LDS buffers, converted once into the dot2 pair layout, splitting
+//    the 64-chunk slots between them so that the x of a stage arrives in one
+//    round trip.  Inputs from outside the chain are staged as soon as the
+//    buffer is free, while earlier stages run; inputs written by an earlier
+//    stage only after the barrier, with device-coherent loads, and the
+//    control wave takes a share of those.
 //
 // Every wait is bounded: past the spin limit the waiter records an error in
 // the workspace and leaves (or, for a compute wave, goes on without waiting),
@@ -81,7 +82,9 @@ struct Shared {
     // working on an earlier stage.
     unsigned progress[kChainComputeWaves];
     unsigned stage_go;  // stages whose x may be staged (inputs written, buffer free)
-    unsigned staged;    // shares of x staging finished, over all staging waves
+    // Stages each staging wave (1 .. kChainStagers - 1) has finished staging;
+    // per wave for the same reason as ``progress``.
+    unsigned staged[kChainStagers];
     unsigned abort;
     unsigned base;
 };
@@ -304,14 +307,14 @@ __device__ __forceinline__ void stage_write(const ChainLaunch& L, int g, int m, 
     *reinterpret_cast<float*>(xg + (size_t)64 * Cp + (size_t)c * 4) = sum;
 }
 
-// This staging wave's share of stage s: slots sid, sid + S, ... (two at a time).
-__device__ void stage_share(const ChainLaunch& L, int s, unsigned char* xb, int lane, int sid) {
+// This staging wave's share of stage s: slots sid, sid + nst, ... (two at a time).
+__device__ void stage_share(const ChainLaunch& L, int s, unsigned char* xb, int lane, int sid, int nst) {
     const ChainStage st = L.stages[s];
     const int n = stage_slots(L, st);
-    for (int k = sid; k < n; k += 2 * kChainStagers) {
+    for (int k = sid; k < n; k += 2 * nst) {
         int g0, m0, g1 = 0, m1 = 0;
         stage_slot(L, st, k, g0, m0);
-        const bool two = stage_slot(L, st, k + kChainStagers, g1, m1);
+        const bool two = stage_slot(L, st, k + nst, g1, m1);
         u32x4_t r0[4], r1[4];
         stage_load(L, g0, m0, lane, r0);
         if (two) stage_load(L, g1, m1, lane, r1);
@@ -320,35 +323,62 @@ __device__ void stage_share(const ChainLaunch& L, int s, unsigned char* xb, int 
     }
 }
 
-// Staging wave sid (1 .. kChainStagers - 1; the control wave is staging wave
-// 0): stage 0 at once, stage t once the control wave has seen the barrier
-// after stage t - 1 (then stage t's inputs are written and the LDS buffer it
-// reuses is free); count each finished share in sh.staged.
+// Bounded LDS wait: true once ``ready()``; false on abort or time-out.
+template <class F>
+__device__ __forceinline__ bool lds_wait(const ChainLaunch& L, Shared& sh, F ready) {
+    unsigned n = 0;
+    bool ok = ready(), ab = lds_load(&sh.abort) != 0u;
+    while (!ok & !ab & (n <= L.spin_limit)) {
+        __builtin_amdgcn_s_sleep(1);
+        ++n;
+        ok = ready();
+        ab = lds_load(&sh.abort) != 0u;
+    }
+    return ok && !ab;
+}
+
+// Staging wave sid (1 .. kChainStagers - 1).  Stage t goes into LDS buffer
+// t & 1, which is free once every compute wave of the workgroup has finished
+// stage t - 2.  When some input of stage t is written by an earlier stage,
+// it can only be staged after the barrier that follows stage t - 1
+// (sh.stage_go >= t); then the control wave takes a share too (all
+// kChainStagers waves split the slots).  When every input comes from outside
+// the chain, the staging waves alone stage it as soon as the buffer is free,
+// while earlier stages still run: off the barrier's path.  sh.staged[sid]
+// counts the stages this wave has staged.
 __device__ void staging_wave(const ChainLaunch& L, Shared& sh, unsigned char* xl, int lane, int sid) {
     for (int t = 0; t < L.num_stages; ++t) {
-        if (t > 0) {
-            unsigned n = 0, r = lds_load(&sh.stage_go), ab = lds_load(&sh.abort);
-            while ((r < (unsigned)t) & (ab == 0u) & (n <= L.spin_limit)) {
-                __builtin_amdgcn_s_sleep(1);
-                ++n;
-                r = lds_load(&sh.stage_go);
-                ab = lds_load(&sh.abort);
-            }
-            if (r < (unsigned)t) return;  // aborted or timed out: the control wave reports it
+        const ChainStage st = L.stages[t];
+        bool ok;
+        if (st.x_internal) {
+            ok = lds_wait(L, sh, [&] { return lds_load(&sh.stage_go) >= (unsigned)t; });
+        } else {
+            ok = t < 2 || lds_wait(L, sh, [&] {
+                     return __builtin_amdgcn_ballot_w64(
+                                lane < kChainComputeWaves &&
+                                lds_load(&sh.progress[lane < kChainComputeWaves ? lane : 0]) + 1u < (unsigned)t) == 0;
+                 });
         }
-        stage_share(L, t, xl + (size_t)(t & 1) * kChainXLdsBytes, lane, sid);
-        if (lane == 0) __hip_atomic_fetch_add(&sh.staged, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (!ok) return;  // aborted or timed out: the control wave reports it
+        if (st.x_internal)
+            stage_share(L, t, xl + (size_t)(t & 1) * kChainXLdsBytes, lane, sid, kChainStagers);
+        else
+            stage_share(L, t, xl + (size_t)(t & 1) * kChainXLdsBytes, lane, sid - 1, kChainStagers - 1);
+        if (lane == 0) __hip_atomic_store(&sh.staged[sid], (unsigned)t + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
 }
 
-// Wait until every staging wave has staged stage t, then release it to the
-// compute waves.
-__device__ __forceinline__ bool release_x(const ChainLaunch& L, Shared& sh, int t) {
-    const unsigned want = (unsigned)kChainStagers * ((unsigned)t + 1u);
-    unsigned n = 0;
-    while (lds_load(&sh.staged) < want) {
-        if (lds_load(&sh.abort) || ++n > L.spin_limit) { set_error(L, sh, 8u); return false; }
-        __builtin_amdgcn_s_sleep(1);
+// Wait until every staging wave has staged stage t (the control wave's own
+// share, if any, is done), then release it to the compute waves.
+__device__ __forceinline__ bool release_x(const ChainLaunch& L, Shared& sh, int lane, int t) {
+    const bool ok = lds_wait(L, sh, [&] {
+        return __builtin_amdgcn_ballot_w64(lane >= 1 && lane < kChainStagers &&
+                                           lds_load(&sh.staged[lane >= 1 && lane < kChainStagers ? lane : 1]) <=
+                                               (unsigned)t) == 0;
+    });
+    if (!ok) {
+        set_error(L, sh, 8u);
+        return false;
     }
     __hip_atomic_store(&sh.x_ready, (unsigned)t + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     return true;
@@ -359,9 +389,8 @@ __device__ void control_wave(const ChainLaunch& L, Shared& sh, unsigned char* xl
     unsigned* my_flag = L.flags + (size_t)wg * kChainLineWords;
     const unsigned* my_go = L.go + (size_t)(wg % kChainGoLines) * kChainLineWords;
     const unsigned base = sh.base;
-    stage_share(L, 0, xl, lane, 0);
-    if (lane == 0) __hip_atomic_fetch_add(&sh.staged, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (!release_x(L, sh, 0)) return;
+    // Stage 0's inputs come from outside the chain: the staging waves have it.
+    if (!release_x(L, sh, lane, 0)) return;
     for (int s = 0; s < L.num_stages; ++s) {
         // Every compute wave of this workgroup has finished stage s (stores complete).
         unsigned n = 0;
@@ -392,11 +421,12 @@ __device__ void control_wave(const ChainLaunch& L, Shared& sh, unsigned char* xl
             __builtin_amdgcn_s_sleep(1);
         }
         // Stage s + 1 may be staged: its inputs are written, and its LDS
-        // buffer (stage s - 1's) is free.
+        // buffer (stage s - 1's) is free.  Inputs from outside the chain are
+        // usually staged by now.
         __hip_atomic_store(&sh.stage_go, (unsigned)s + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        stage_share(L, s + 1, xl + (size_t)((s + 1) & 1) * kChainXLdsBytes, lane, 0);
-        if (lane == 0) __hip_atomic_fetch_add(&sh.staged, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (!release_x(L, sh, s + 1)) return;
+        if (L.stages[s + 1].x_internal)
+            stage_share(L, s + 1, xl + (size_t)((s + 1) & 1) * kChainXLdsBytes, lane, 0, kChainStagers);
+        if (!release_x(L, sh, lane, s + 1)) return;
     }
 }
 
@@ -487,7 +517,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainStage* 
         sh.x_ready = 0;
         for (int i = 0; i < kChainComputeWaves; ++i) sh.progress[i] = 0;
         sh.stage_go = 0;
-        sh.staged = 0;
+        for (int i = 0; i < kChainStagers; ++i) sh.staged[i] = 0;
         sh.abort = 0;
         sh.base = flag_load(L.flags + (size_t)blockIdx.x * kChainLineWords);
     }
