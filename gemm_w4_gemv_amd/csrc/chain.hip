@@ -158,8 +158,7 @@ __device__ __forceinline__ Work advance(const ChainLaunch& L, Work w, int v, int
 // an empty buffer range, which returns zeros without touching memory: the
 // same loads are issued on every path, so the compiler's wait counts for the
 // first tile stay exact.
-__device__ __forceinline__ void issue(const ChainLaunch& L, const Work& w, bool dummy, int lane, TileRegs& R) {
-    const ChainGemv G = L.gemvs[w.g];
+__device__ __forceinline__ void issue(const ChainGemv& G, const Work& w, bool dummy, int lane, TileRegs& R) {
     const int C = G.C, N = G.N, Gr = C >> 2, sp = G.sp, sh = seg_shift(sp);
     const uint32_t row_bytes = (uint32_t)C * 16u;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(G.qw, dummy ? 0u : (uint32_t)N * row_bytes);
@@ -469,34 +468,47 @@ __device__ void compute_wave(const ChainLaunch& L, Shared& sh, const unsigned ch
     // Nothing but the tile in R is in flight at the loop head, so the
     // compiler's waits there are exact.
     TileRegs R;
-    issue(L, a, false, lane, R);
+    ChainGemv Ga = L.gemvs[a.g];
+    issue(Ga, a, false, lane, R);
     for (;;) {
+        // The next work and its table entries first: their scalar loads are
+        // then in flight during this tile's math, not after it.
+        const Work b = advance(L, a, v, W);
+        const bool has_b = b.s < L.num_stages;
+        const bool near = has_b && b.s <= a.s + 1;
+        const ChainGemv Gb = L.gemvs[has_b ? b.g : a.g];
+        const bool acked = !has_b || L.stages[b.s].internal_through != L.stages[a.s].internal_through;
         if (x_stage != a.s) {
             wait_x(a.s);
             x_stage = a.s;
         }
-        const ChainGemv G = L.gemvs[a.g];
-        compute(G, a, lane, R, xl + (size_t)(a.s & 1) * kChainXLdsBytes + G.x_lds);
+        compute(Ga, a, lane, R, xl + (size_t)(a.s & 1) * kChainXLdsBytes + Ga.x_lds);
         // Keep the next tile's loads below this tile's stores.
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("" ::: "memory");
-        const Work b = advance(L, a, v, W);
-        const bool has_b = b.s < L.num_stages;
-        const bool near = has_b && b.s <= a.s + 1;
-        if (near) issue(L, b, false, lane, R);
+        if (near) issue(Gb, b, false, lane, R);
         if (b.s != a.s) {
-            if (near)
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTileLoads));  // only the loads just issued may be pending
-            else
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            // Stages a.s .. b.s - 1 are done.  If one of stages a.s + 1 ..
+            // b.s reads outputs of the chain, the stores must be complete
+            // before the report; otherwise nothing in this launch reads them
+            // after this barrier (outputs never overlap, and inputs were
+            // staged before the math), and the launch's end makes them
+            // visible.
+            if (acked) {
+                if (near)
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTileLoads));  // only the loads just issued may be pending
+                else
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            }
             report(b.s);
         }
         if (!has_b) break;
         if (!near) {
             wait_x(b.s - 1);
-            issue(L, b, false, lane, R);
+            issue(Gb, b, false, lane, R);
         }
         a = b;
+        Ga = Gb;
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }

@@ -30,6 +30,10 @@ struct ChainStage {
     int ngemv;
     int tiles;       // total tiles of the stage's GEMVs
     int x_internal;  // 1: some input of the stage is written by an earlier stage
+    // Stages u <= this one with x_internal: the barrier after stage r must
+    // find every earlier output written only when stage r + 1 reads outputs
+    // of the chain.
+    int internal_through;
 };
 
 constexpr int kChainThreads = 1024;  // 16 waves: 1 control, kChainComputeWaves compute, the rest staging

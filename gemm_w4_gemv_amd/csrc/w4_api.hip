@@ -264,7 +264,7 @@ W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* wor
     for (int i = 0; i < count; ++i) {
         const w4_gemv_desc& d = descs[i];
         if (i == 0 || d.stage != descs[i - 1].stage) {
-            stages.push_back({i, 0, 0, 0});
+            stages.push_back({i, 0, 0, 0, 0});
             x_bytes = 0;
         }
         w4::ChainStage& st = stages.back();
@@ -291,6 +291,8 @@ W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* wor
         st.tiles += (d.N + rows_per_tile - 1) / rows_per_tile;
         st.ngemv += 1;
     }
+    for (size_t t = 1; t < stages.size(); ++t)
+        stages[t].internal_through = stages[t - 1].internal_through + stages[t].x_internal;
     int occ = 0, cus = 0, dev = 0;
     hipError_t err = w4::chain_occupancy(&occ);
     if (err == hipSuccess) err = hipGetDevice(&dev);
