@@ -391,6 +391,8 @@ __device__ void control_wave(const ChainLaunch& L, Shared& sh, unsigned char* xl
     // Stage 0's inputs come from outside the chain: the staging waves have it.
     if (!release_x(L, sh, lane, 0)) return;
     for (int s = 0; s < L.num_stages; ++s) {
+        // Read early: the scalar load completes during the waits below.
+        const bool next_internal = s + 1 < L.num_stages && L.stages[s + 1].x_internal;
         // Every compute wave of this workgroup has finished stage s (stores complete).
         unsigned n = 0;
         while (__builtin_amdgcn_ballot_w64(lane < kChainComputeWaves &&
@@ -404,6 +406,8 @@ __device__ void control_wave(const ChainLaunch& L, Shared& sh, unsigned char* xl
         if (s + 1 >= L.num_stages) break;  // nothing waits for the last stage
 
         if (wg == 0) {  // coordinator: every workgroup's stage s, then publish
+            // Each lane polls its workgroups' flags (lane, lane + 64, ...) one
+            // after another (measured faster than polling them all each round).
             for (int w = lane; w < P; w += kWave) {
                 unsigned m = 0;
                 while (older(flag_load(L.flags + (size_t)w * kChainLineWords), target)) {
@@ -423,7 +427,7 @@ __device__ void control_wave(const ChainLaunch& L, Shared& sh, unsigned char* xl
         // buffer (stage s - 1's) is free.  Inputs from outside the chain are
         // usually staged by now.
         __hip_atomic_store(&sh.stage_go, (unsigned)s + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (L.stages[s + 1].x_internal)
+        if (next_internal)
             stage_share(L, s + 1, xl + (size_t)((s + 1) & 1) * kChainXLdsBytes, lane, 0, kChainStagers);
         if (!release_x(L, sh, lane, s + 1)) return;
     }
