@@ -64,7 +64,7 @@ SIGNATURES = {
     "w4_graph_end": (_i32, [_vp, ctypes.POINTER(_vp)]),
     "w4_graph_replay": (_i32, [_vp, _vp]),
     "w4_graph_destroy": (None, [_vp]),
-    "w4_chain_workspace_bytes": (_sz, [_i32, _i32]),
+    "w4_chain_workspace_bytes": (_sz, [_vp, _i32]),
     "w4_chain_create": (_i32, [ctypes.POINTER(GemvDesc), _i32, _vp, _sz, ctypes.POINTER(_vp)]),
     "w4_chain_run": (_i32, [_vp, _vp]),
     "w4_chain_error": (_i32, [_vp, ctypes.POINTER(ctypes.c_uint32)]),
@@ -248,8 +248,24 @@ def w4_graph_destroy(graph: W4Graph) -> None:
     graph.destroy()
 
 
-def w4_chain_workspace_bytes(count: int, num_stages: int) -> int:
-    return lib.w4_chain_workspace_bytes(count, num_stages)
+def _chain_descs(gemvs):
+    descs = (GemvDesc * len(gemvs))()
+    for i, g in enumerate(gemvs):
+        K = g["x"].numel()
+        N, pq, ps, pz = _int4_weight(g["qw"], g["s"], g["z"], K, INT4_GROUP)
+        if g["y"].numel() != N:
+            raise ValueError(f"gemv {i}: y must hold N = {N} values")
+        descs[i] = GemvDesc(_dev(g["x"], "x", _BF16), pq, ps, pz, _dev(g["y"], "y", _BF16), K, N, int(g["stage"]), 0)
+    return descs
+
+
+def w4_chain_workspace_bytes(gemvs) -> int:
+    """Workspace bytes the chain of ``gemvs`` (as for w4_chain_create) needs."""
+    descs = _chain_descs(gemvs)
+    n = lib.w4_chain_workspace_bytes(ctypes.cast(descs, _vp), len(gemvs))
+    if n == 0:  # invalid descriptors; w4_last_error says why
+        raise W4Error(7, "w4_chain_workspace_bytes")
+    return n
 
 
 class W4Chain:
@@ -281,14 +297,8 @@ def w4_chain_create(gemvs, workspace: torch.Tensor) -> W4Chain:
     """Plan a chain.  ``gemvs``: sequence of dicts with device tensors ``x`` (bf16 [K]),
     ``qw`` (int32 [N, K/8]), ``s``, ``z`` (fp16 [N, K/128]), ``y`` (bf16 [N]) and an int
     ``stage`` (non-decreasing).  ``workspace``: device tensor of at least
-    w4_chain_workspace_bytes(len(gemvs), number of stages) bytes."""
-    descs = (GemvDesc * len(gemvs))()
-    for i, g in enumerate(gemvs):
-        K = g["x"].numel()
-        N, pq, ps, pz = _int4_weight(g["qw"], g["s"], g["z"], K, INT4_GROUP)
-        if g["y"].numel() != N:
-            raise ValueError(f"gemv {i}: y must hold N = {N} values")
-        descs[i] = GemvDesc(_dev(g["x"], "x", _BF16), pq, ps, pz, _dev(g["y"], "y", _BF16), K, N, int(g["stage"]), 0)
+    w4_chain_workspace_bytes(gemvs) bytes."""
+    descs = _chain_descs(gemvs)
     nbytes = workspace.numel() * workspace.element_size()
     h = _vp()
     _check(lib.w4_chain_create(descs, len(gemvs), _dev(workspace, "workspace", (workspace.dtype,)), nbytes,

@@ -61,7 +61,6 @@ namespace {
 // are 128 (q % sp) + l and + l + 64, in groups 32 (q % sp) + (l + 64 i) / 4.
 constexpr int kSlotRows = kChainTileRows;
 constexpr int kSlotLanes = kWave / kSlotRows;  // lanes per slot-row after the row reduction
-constexpr int kTileLoads = 3 * kSlotRows;     // weight loads (2 per slot-row) and scale/zero loads (1)
 
 struct TileRegs {
     u32x4_t w[2 * kSlotRows];  // slot (q, i) in w[2 q + i]
@@ -75,19 +74,22 @@ struct Work {
 };
 
 struct Shared {
-    unsigned x_ready;  // stages whose x is staged and whose predecessors are complete
-    // Stages each compute wave has finished (its stores complete).  One word
-    // per wave, not a shared count: a wave with no tiles in the next stages
-    // reports several at once, and a sum would then run ahead of waves still
-    // working on an earlier stage.
+    // Stages each compute wave has finished with (its LDS x no longer
+    // needed).  One word per wave, not a shared count: a wave with no tiles
+    // in the next stages reports several at once, and a sum would then run
+    // ahead of waves still working on an earlier stage.
     unsigned progress[kChainComputeWaves];
-    unsigned stage_go;  // stages whose x may be staged (inputs written, buffer free)
-    // Stages each staging wave (1 .. kChainStagers - 1) has finished staging;
-    // per wave for the same reason as ``progress``.
+    // Stages each staging wave has staged; per wave for the same reason.
     unsigned staged[kChainStagers];
     unsigned abort;
-    unsigned base;
+    unsigned base;      // launches this workgroup has run before this one
+    unsigned tag_base;  // (base * num_stages) mod 65535
 };
+
+// Tag of the outputs stage t writes in this launch: never 0 (the value the
+// mirrors are cleared to), and different from the previous launch's tag for
+// the same stage as long as there are fewer than 65535 stages.
+__device__ __forceinline__ unsigned stage_tag(const Shared& sh, int t) { return (sh.tag_base + (unsigned)t) % 65535u + 1u; }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -100,8 +102,6 @@ __device__ __forceinline__ int seg_shift(int sp) { return sp == 1 ? 0 : (sp == 2
 __device__ __forceinline__ unsigned lds_load(const unsigned* p) {
     return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-
-__device__ __forceinline__ bool older(unsigned a, unsigned b) { return (int)(a - b) < 0; }
 
 __device__ __forceinline__ void set_error(const ChainLaunch& L, Shared& sh, unsigned bit) {
     __hip_atomic_fetch_or(L.err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -214,7 +214,7 @@ __device__ __forceinline__ float slot(const TileRegs& R, int q, int i, int lane,
 // With a single segment every row of the tile uses the lane's same two x
 // chunks, read once per tile.
 __device__ __forceinline__ void compute(const ChainGemv& G, const Work& w, int lane, const TileRegs& R,
-                                        const unsigned char* xg) {
+                                        const unsigned char* xg, unsigned tag) {
     const int sp = G.sp, Cp = chain_x_chunks(G.C);
     const uint32_t bias = vgpr_const(kInt4BiasPair);
     float acc[kSlotRows];
@@ -241,8 +241,14 @@ __device__ __forceinline__ void compute(const ChainGemv& G, const Work& w, int l
     if (sp == 4) total += __shfl_xor(total, 2 * kSlotLanes, kWave);
     const int j = (lane / kSlotLanes) >> seg_shift(sp);  // row of the tile this lane's total belongs to
     if ((lane & (kSlotLanes * sp - 1)) == 0 && j < w.nrows) {
+        const uint16_t v = f32_to_bf16(total);
         const __amdgpu_buffer_rsrc_t ry = make_rsrc(G.y, (uint32_t)G.N * 2u);
-        buf_store_u16_coherent(f32_to_bf16(total), ry, (uint32_t)(w.row + j) * 2u, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(v, ry, (int)((w.row + j) * 2), 0, 0);
+        if (G.ym) {  // the tagged copy a later GEMV polls for: one 32-bit device-coherent store
+            const __amdgpu_buffer_rsrc_t rm = make_rsrc(G.ym, (uint32_t)G.N * 4u);
+            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v | (tag << 16), rm, (int)((w.row + j) * 4), 0,
+                                                  kAuxDeviceCoherent);
+        }
     }
 }
 
@@ -277,13 +283,45 @@ __device__ __forceinline__ void stage_load(const ChainLaunch& L, int g, int m, i
     const ChainGemv& G = L.gemvs[g];
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(G.x, (uint32_t)G.C * 64u);
     const uint32_t c = (uint32_t)min(m * kWave + lane, G.C - 1);
-    if (G.x_internal) {  // written by an earlier stage: device-coherent loads
 #pragma unroll
-        for (int p = 0; p < 4; ++p) raw[p] = buf_load_b128_coherent(rx, c * 64u + 16u * p, 0);
-    } else {
+    for (int p = 0; p < 4; ++p) raw[p] = buf_load_b128<0>(rx, c * 64u + 16u * p, 0);
+}
+
+// x of chunk m * 64 + lane of GEMV g from its producer's tagged output:
+// poll (device-coherent loads, bounded) until all 32 words carry the
+// producer stage's tag, then keep the BF16 halves.  False on time-out.
+__device__ __forceinline__ bool stage_poll(const ChainLaunch& L, Shared& sh, int g, int m, int lane, u32x4_t raw[4]) {
+    const ChainGemv& G = L.gemvs[g];
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(G.xm, (uint32_t)G.C * 128u);
+    const unsigned want = stage_tag(sh, G.xm_stage);
+    const int c = m * kWave + lane;
+    bool done = c >= G.C;  // padding chunks are staged as zeros
+    u32x4_t w[8];
+    unsigned n = 0;
+    for (;;) {
+        if (!done) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) raw[p] = buf_load_b128<0>(rx, c * 64u + 16u * p, 0);
+            for (int p = 0; p < 8; ++p) w[p] = buf_load_b128_coherent(rm, (uint32_t)c * 128u + 16u * p, 0);
+            bool ok = true;
+#pragma unroll
+            for (int p = 0; p < 8; ++p)
+                ok &= ((w[p].x >> 16) == want) & ((w[p].y >> 16) == want) & ((w[p].z >> 16) == want) &
+                      ((w[p].w >> 16) == want);
+            done = ok;
+        }
+        if (__builtin_amdgcn_ballot_w64(!done) == 0) break;
+        if (lds_load(&sh.abort) || ++n > L.spin_limit) return false;
+        __builtin_amdgcn_s_sleep(8);
     }
+    // Word pairs (x_2i, x_2i+1) from the low halves of words 2i and 2i + 1.
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        raw[p].x = __builtin_amdgcn_perm(w[2 * p].y, w[2 * p].x, 0x05040100u);
+        raw[p].y = __builtin_amdgcn_perm(w[2 * p].w, w[2 * p].z, 0x05040100u);
+        raw[p].z = __builtin_amdgcn_perm(w[2 * p + 1].y, w[2 * p + 1].x, 0x05040100u);
+        raw[p].w = __builtin_amdgcn_perm(w[2 * p + 1].w, w[2 * p + 1].z, 0x05040100u);
+    }
+    return true;
 }
 
 __device__ __forceinline__ void stage_write(const ChainLaunch& L, int g, int m, int lane, const u32x4_t raw[4],
@@ -306,20 +344,30 @@ __device__ __forceinline__ void stage_write(const ChainLaunch& L, int g, int m, 
     *reinterpret_cast<float*>(xg + (size_t)64 * Cp + (size_t)c * 4) = sum;
 }
 
-// This staging wave's share of stage s: slots sid, sid + nst, ... (two at a time).
-__device__ void stage_share(const ChainLaunch& L, int s, unsigned char* xb, int lane, int sid, int nst) {
+// This staging wave's share of stage s: slots sid, sid + kChainStagers, ...
+// External inputs two slots at a time; inputs from earlier GEMVs one at a
+// time, polled.  False if a poll timed out.
+__device__ bool stage_share(const ChainLaunch& L, Shared& sh, int s, unsigned char* xb, int lane, int sid) {
     const ChainStage st = L.stages[s];
     const int n = stage_slots(L, st);
-    for (int k = sid; k < n; k += 2 * nst) {
+    for (int k = sid; k < n;) {
         int g0, m0, g1 = 0, m1 = 0;
         stage_slot(L, st, k, g0, m0);
-        const bool two = stage_slot(L, st, k + nst, g1, m1);
         u32x4_t r0[4], r1[4];
+        if (L.gemvs[g0].x_internal) {
+            if (!stage_poll(L, sh, g0, m0, lane, r0)) return false;
+            stage_write(L, g0, m0, lane, r0, xb);
+            k += kChainStagers;
+            continue;
+        }
+        const bool two = stage_slot(L, st, k + kChainStagers, g1, m1) && !L.gemvs[g1].x_internal;
         stage_load(L, g0, m0, lane, r0);
         if (two) stage_load(L, g1, m1, lane, r1);
         stage_write(L, g0, m0, lane, r0, xb);
         if (two) stage_write(L, g1, m1, lane, r1, xb);
+        k += two ? 2 * kChainStagers : kChainStagers;
     }
+    return true;
 }
 
 // Bounded LDS wait: true once ``ready()``; false on abort or time-out.
@@ -336,107 +384,40 @@ __device__ __forceinline__ bool lds_wait(const ChainLaunch& L, Shared& sh, F rea
     return ok && !ab;
 }
 
-// Staging wave sid (1 .. kChainStagers - 1).  Stage t goes into LDS buffer
+// Staging wave sid (0 .. kChainStagers - 1).  Stage t goes into LDS buffer
 // t & 1, which is free once every compute wave of the workgroup has finished
-// stage t - 2.  When some input of stage t is written by an earlier stage,
-// it can only be staged after the barrier that follows stage t - 1
-// (sh.stage_go >= t); then the control wave takes a share too (all
-// kChainStagers waves split the slots).  When every input comes from outside
-// the chain, the staging waves alone stage it as soon as the buffer is free,
-// while earlier stages still run: off the barrier's path.  sh.staged[sid]
-// counts the stages this wave has staged.
+// stage t - 2; the staging waves split its 64-chunk slots.  An input from
+// outside the chain is loaded as soon as the buffer is free (while earlier
+// stages still run); an input that is an earlier GEMV's output is polled
+// from that GEMV's tagged copy until every word carries its writer's tag,
+// so a stage waits for exactly the outputs it reads and for nothing else.
+// sh.staged[sid] counts the stages this wave has staged.
 __device__ void staging_wave(const ChainLaunch& L, Shared& sh, unsigned char* xl, int lane, int sid) {
     for (int t = 0; t < L.num_stages; ++t) {
-        const ChainStage st = L.stages[t];
-        bool ok;
-        if (st.x_internal) {
-            ok = lds_wait(L, sh, [&] { return lds_load(&sh.stage_go) >= (unsigned)t; });
-        } else {
-            ok = t < 2 || lds_wait(L, sh, [&] {
-                     return __builtin_amdgcn_ballot_w64(
-                                lane < kChainComputeWaves &&
-                                lds_load(&sh.progress[lane < kChainComputeWaves ? lane : 0]) + 1u < (unsigned)t) == 0;
-                 });
+        // Buffer free: every compute wave here is past stage t - 2.  A stage
+        // that reads earlier outputs also waits until this workgroup's own
+        // part of stage t - 1 is done: by then the other workgroups' parts
+        // are mostly done too, so the polls that follow are few (polling
+        // from the start of stage t - 1 would load the inputs over and over
+        // while the weights stream).
+        const unsigned need = L.stages[t].x_internal ? (unsigned)t : (unsigned)max(t - 1, 0);
+        const bool ok = need == 0 || lds_wait(L, sh, [&] {
+                            return __builtin_amdgcn_ballot_w64(
+                                       lane < kChainComputeWaves &&
+                                       lds_load(&sh.progress[lane < kChainComputeWaves ? lane : 0]) < need) == 0;
+                        });
+        if (!ok || !stage_share(L, sh, t, xl + (size_t)(t & 1) * kChainXLdsBytes, lane, sid)) {
+            set_error(L, sh, 8u);
+            return;
         }
-        if (!ok) return;  // aborted or timed out: the control wave reports it
-        if (st.x_internal)
-            stage_share(L, t, xl + (size_t)(t & 1) * kChainXLdsBytes, lane, sid, kChainStagers);
-        else
-            stage_share(L, t, xl + (size_t)(t & 1) * kChainXLdsBytes, lane, sid - 1, kChainStagers - 1);
         if (lane == 0) __hip_atomic_store(&sh.staged[sid], (unsigned)t + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-}
-
-// Wait until every staging wave has staged stage t (the control wave's own
-// share, if any, is done), then release it to the compute waves.
-__device__ __forceinline__ bool release_x(const ChainLaunch& L, Shared& sh, int lane, int t) {
-    const bool ok = lds_wait(L, sh, [&] {
-        return __builtin_amdgcn_ballot_w64(lane >= 1 && lane < kChainStagers &&
-                                           lds_load(&sh.staged[lane >= 1 && lane < kChainStagers ? lane : 1]) <=
-                                               (unsigned)t) == 0;
-    });
-    if (!ok) {
-        set_error(L, sh, 8u);
-        return false;
-    }
-    __hip_atomic_store(&sh.x_ready, (unsigned)t + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    return true;
-}
-
-__device__ void control_wave(const ChainLaunch& L, Shared& sh, unsigned char* xl, int lane) {
-    const int wg = blockIdx.x, P = L.workers;
-    unsigned* my_flag = L.flags + (size_t)wg * kChainLineWords;
-    const unsigned* my_go = L.go + (size_t)(wg % kChainGoLines) * kChainLineWords;
-    const unsigned base = sh.base;
-    // Stage 0's inputs come from outside the chain: the staging waves have it.
-    if (!release_x(L, sh, lane, 0)) return;
-    for (int s = 0; s < L.num_stages; ++s) {
-        // Read early: the scalar load completes during the waits below.
-        const bool next_internal = s + 1 < L.num_stages && L.stages[s + 1].x_internal;
-        // Every compute wave of this workgroup has finished stage s (stores complete).
-        unsigned n = 0;
-        while (__builtin_amdgcn_ballot_w64(lane < kChainComputeWaves &&
-                                           lds_load(&sh.progress[lane < kChainComputeWaves ? lane : 0]) <=
-                                               (unsigned)s) != 0) {
-            if (lds_load(&sh.abort) || ++n > L.spin_limit) { set_error(L, sh, 4u); return; }
-            __builtin_amdgcn_s_sleep(1);
-        }
-        const unsigned target = base + (unsigned)s + 1u;
-        if (lane == 0) flag_store(my_flag, target);
-        if (s + 1 >= L.num_stages) break;  // nothing waits for the last stage
-
-        if (wg == 0) {  // coordinator: every workgroup's stage s, then publish
-            // Each lane polls its workgroups' flags (lane, lane + 64, ...) one
-            // after another (measured faster than polling them all each round).
-            for (int w = lane; w < P; w += kWave) {
-                unsigned m = 0;
-                while (older(flag_load(L.flags + (size_t)w * kChainLineWords), target)) {
-                    if (++m > L.spin_limit) { set_error(L, sh, 1u); break; }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-            }
-            if (lds_load(&sh.abort)) return;
-            if (lane < kChainGoLines) flag_store(L.go + (size_t)lane * kChainLineWords, target);
-        }
-        n = 0;
-        while (older(flag_load(my_go), target)) {
-            if (++n > L.spin_limit) { set_error(L, sh, 2u); return; }
-            __builtin_amdgcn_s_sleep(1);
-        }
-        // Stage s + 1 may be staged: its inputs are written, and its LDS
-        // buffer (stage s - 1's) is free.  Inputs from outside the chain are
-        // usually staged by now.
-        __hip_atomic_store(&sh.stage_go, (unsigned)s + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (next_internal)
-            stage_share(L, s + 1, xl + (size_t)((s + 1) & 1) * kChainXLdsBytes, lane, 0, kChainStagers);
-        if (!release_x(L, sh, lane, s + 1)) return;
     }
 }
 
 // --------------------------------------------------------------- compute wave
 __device__ void compute_wave(const ChainLaunch& L, Shared& sh, const unsigned char* xl, int lane, int wi, int v,
                              int W) {
-    // Report stages < upto done; the caller has made its stores complete.
+    // Report stages < upto done with (their LDS x is no longer read).
     auto report = [&](int upto) {
         if (lane == 0)
             __hip_atomic_store(&sh.progress[wi], (unsigned)upto, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -446,13 +427,18 @@ __device__ void compute_wave(const ChainLaunch& L, Shared& sh, const unsigned ch
     // so): leaving the tile loop early instead makes the compiler's wait-count
     // analysis assume that the prefetched tiles were issued last, and wait for
     // all of them before every tile's math.
+    auto staged = [&](int s) {
+        return __builtin_amdgcn_ballot_w64(lane < kChainStagers &&
+                                           lds_load(&sh.staged[lane < kChainStagers ? lane : 0]) <= (unsigned)s) == 0;
+    };
     auto wait_x = [&](int s) {
-        unsigned n = 0, r = lds_load(&sh.x_ready), ab = lds_load(&sh.abort);
-        while ((r <= (unsigned)s) & (ab == 0u) & (n <= L.spin_limit)) {
+        unsigned n = 0;
+        bool r = staged(s), ab = lds_load(&sh.abort) != 0u;
+        while (!r & !ab & (n <= L.spin_limit)) {
             __builtin_amdgcn_s_sleep(1);
             ++n;
-            r = lds_load(&sh.x_ready);
-            ab = lds_load(&sh.abort);
+            r = staged(s);
+            ab = lds_load(&sh.abort) != 0u;
         }
     };
 
@@ -463,14 +449,13 @@ __device__ void compute_wave(const ChainLaunch& L, Shared& sh, const unsigned ch
     if (a.s >= L.num_stages) return;
 
     // One tile in flight per wave: compute it, store its rows, then issue the
-    // next tile's loads.  The stores go out before those loads, so at the end
-    // of a stage vmcnt(kTileLoads) (the loads just issued) proves them
-    // complete while the next stage's weights are already on their way across
-    // the stage barrier.  A tile two or more stages ahead is not issued until
-    // the stage before it is released: weights then reach the memory system
-    // in stage order, and a stage's tiles do not queue behind later stages'.
+    // next tile's loads, which are then on their way while the next stage's
+    // inputs arrive.  A tile two or more stages ahead is not issued until the
+    // stage before it is staged: weights then reach the memory system in
+    // stage order, and a stage's tiles do not queue behind later stages'.
     // Nothing but the tile in R is in flight at the loop head, so the
-    // compiler's waits there are exact.
+    // compiler's waits there are exact.  No wave ever waits for its own
+    // stores: readers poll the tagged outputs.
     TileRegs R;
     ChainGemv Ga = L.gemvs[a.g];
     issue(Ga, a, false, lane, R);
@@ -481,31 +466,16 @@ __device__ void compute_wave(const ChainLaunch& L, Shared& sh, const unsigned ch
         const bool has_b = b.s < L.num_stages;
         const bool near = has_b && b.s <= a.s + 1;
         const ChainGemv Gb = L.gemvs[has_b ? b.g : a.g];
-        const bool acked = !has_b || L.stages[b.s].internal_through != L.stages[a.s].internal_through;
         if (x_stage != a.s) {
             wait_x(a.s);
             x_stage = a.s;
         }
-        compute(Ga, a, lane, R, xl + (size_t)(a.s & 1) * kChainXLdsBytes + Ga.x_lds);
+        compute(Ga, a, lane, R, xl + (size_t)(a.s & 1) * kChainXLdsBytes + Ga.x_lds, stage_tag(sh, a.s));
         // Keep the next tile's loads below this tile's stores.
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("" ::: "memory");
         if (near) issue(Gb, b, false, lane, R);
-        if (b.s != a.s) {
-            // Stages a.s .. b.s - 1 are done.  If one of stages a.s + 1 ..
-            // b.s reads outputs of the chain, the stores must be complete
-            // before the report; otherwise nothing in this launch reads them
-            // after this barrier (outputs never overlap, and inputs were
-            // staged before the math), and the launch's end makes them
-            // visible.
-            if (acked) {
-                if (near)
-                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTileLoads));  // only the loads just issued may be pending
-                else
-                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-            }
-            report(b.s);
-        }
+        if (b.s != a.s) report(b.s);
         if (!has_b) break;
         if (!near) {
             wait_x(b.s - 1);
@@ -530,22 +500,23 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainStage* 
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     if (tid == 0) {
-        sh.x_ready = 0;
         for (int i = 0; i < kChainComputeWaves; ++i) sh.progress[i] = 0;
-        sh.stage_go = 0;
         for (int i = 0; i < kChainStagers; ++i) sh.staged[i] = 0;
         sh.abort = 0;
-        sh.base = flag_load(L.flags + (size_t)blockIdx.x * kChainLineWords);
+        sh.base = L.counters[(size_t)blockIdx.x * kChainLineWords];
+        sh.tag_base = (sh.base % 65535u) * ((unsigned)L.num_stages % 65535u) % 65535u;
     }
-    __syncthreads();  // the only workgroup barrier: roles split below
-    if (wave == 0) {
-        control_wave(L, sh, xl, lane);
-    } else if (wave <= kChainComputeWaves) {
+    __syncthreads();
+    if (wave >= 1 && wave <= kChainComputeWaves) {
         const int W = L.workers * kChainComputeWaves;
         compute_wave(L, sh, xl, lane, wave - 1, uniform((int)blockIdx.x * kChainComputeWaves + (wave - 1)), W);
     } else {
-        staging_wave(L, sh, xl, lane, wave - kChainComputeWaves);
+        staging_wave(L, sh, xl, lane, wave == 0 ? 0 : wave - kChainComputeWaves);
     }
+    // Every wave has left its loop (all waits are bounded): count the launch.
+    // The next launch of the chain reads the counter only after this one ends.
+    __syncthreads();
+    if (tid == 0) L.counters[(size_t)blockIdx.x * kChainLineWords] = sh.base + 1u;
 }
 
 }  // namespace

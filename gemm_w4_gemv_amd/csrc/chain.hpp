@@ -1,6 +1,7 @@
 // Tables of the persistent decode-chain kernel, shared by the host planner
 // (w4_api.hip) and the kernel (chain.hip).  They live in the caller's
-// workspace, written once by w4_chain_create.
+// workspace, written once by w4_chain_create, beside the tagged copies of
+// the outputs that later GEMVs read.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,7 +21,15 @@ struct ChainGemv {
     int sp;          // segments of 128 chunks per row: 1 (K <= 4096), 2 (K <= 8192) or 4 (K <= 16384)
     int tile0;       // first tile of this GEMV in its stage (tiles are kChainTileRows / sp rows)
     int x_lds;       // byte offset of this GEMV's staged x in its LDS buffer
-    int x_internal;  // 1: x is written by an earlier stage of the chain
+    int x_internal;  // 1: x is the output of an earlier GEMV of the chain (read from xm)
+    // Tagged outputs: word r = bf16 y[r] | tag << 16, the tag naming the
+    // launch and stage that wrote it.  ym: where this GEMV writes its own
+    // (null when no GEMV reads its output); xm: its producer's, read instead
+    // of x (null when x comes from outside the chain).
+    unsigned* ym;
+    const unsigned* xm;
+    int xm_stage;  // stage index of xm's writer (its tags)
+    int reserved;
 };
 
 // GEMVs gemv0 .. gemv0 + ngemv - 1 form one stage: they run concurrently;
@@ -29,20 +38,15 @@ struct ChainStage {
     int gemv0;
     int ngemv;
     int tiles;       // total tiles of the stage's GEMVs
-    int x_internal;  // 1: some input of the stage is written by an earlier stage
-    // Stages u <= this one with x_internal: the barrier after stage r must
-    // find every earlier output written only when stage r + 1 reads outputs
-    // of the chain.
-    int internal_through;
+    int x_internal;  // 1: some input of the stage is an output of an earlier GEMV
 };
 
 constexpr int kChainThreads = 1024;  // 16 waves: 1 control, kChainComputeWaves compute, the rest staging
 constexpr int kChainComputeWaves = 8;
-constexpr int kChainStagers = 16 - kChainComputeWaves;  // staging waves, the control wave included
+constexpr int kChainStagers = 16 - kChainComputeWaves;  // staging waves
 constexpr int kChainMaxWorkers = 1024;
-constexpr int kChainGoLines = 64;
 constexpr int kChainTileRows = 4;     // slot-rows per compute-wave tile: 4 / sp rows of a GEMV
-constexpr int kChainLineWords = 32;    // one 128-byte line per flag
+constexpr int kChainLineWords = 32;    // one 128-byte line per launch counter
 constexpr int kChainMaxC = 512;        // K <= 16384
 constexpr int kChainXLdsBytes = 65536; // staged x (pairs + chunk sums) of one stage; two buffers
 
@@ -53,21 +57,23 @@ __host__ __device__ inline int chain_x_chunks(int C) { return (C + 127) / 128 * 
 // FP32 sum per (padded) chunk.
 __host__ __device__ inline int chain_x_lds_bytes(int C) { return 68 * chain_x_chunks(C); }
 
-// Workspace layout: [error line][worker flag lines][go lines][stages][gemvs].
+// Workspace layout: [error line][per-workgroup launch counter lines][stages]
+// [gemvs][tagged outputs, mirror_words 32-bit words].
 struct ChainLayout {
-    size_t err, flags, go, stages, gemvs, total;
+    size_t err, counters, stages, gemvs, mirrors, total;
 };
 
-inline ChainLayout chain_layout(int num_gemvs, int num_stages) {
+inline ChainLayout chain_layout(int num_gemvs, int num_stages, size_t mirror_words) {
     const size_t line = kChainLineWords * 4;
     ChainLayout l;
     l.err = 0;
-    l.flags = line;
-    l.go = l.flags + (size_t)kChainMaxWorkers * line;
-    l.stages = l.go + (size_t)kChainGoLines * line;
+    l.counters = line;
+    l.stages = l.counters + (size_t)kChainMaxWorkers * line;
     l.gemvs = l.stages + (size_t)num_stages * sizeof(ChainStage);
     l.gemvs = (l.gemvs + 63) & ~(size_t)63;
-    l.total = l.gemvs + (size_t)num_gemvs * sizeof(ChainGemv);
+    l.mirrors = l.gemvs + (size_t)num_gemvs * sizeof(ChainGemv);
+    l.mirrors = (l.mirrors + 255) & ~(size_t)255;
+    l.total = l.mirrors + mirror_words * 4;
     return l;
 }
 
@@ -75,8 +81,7 @@ struct ChainLaunch {
     const ChainStage* stages;
     const ChainGemv* gemvs;
     unsigned* err;
-    unsigned* flags;
-    unsigned* go;
+    unsigned* counters;  // one line per workgroup: launches it has run
     int num_stages;
     int workers;  // workgroups, one per compute unit
     unsigned spin_limit;

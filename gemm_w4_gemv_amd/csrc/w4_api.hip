@@ -207,21 +207,21 @@ struct w4_chain {
     w4::ChainLaunch launch;
 };
 
-W4_API size_t w4_chain_workspace_bytes(int count, int num_stages) {
-    if (count <= 0 || num_stages <= 0) return 0;
-    return w4::chain_layout(count, num_stages).total;
-}
+namespace {
 
-W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* workspace, size_t workspace_bytes,
-                                 w4_chain_t* chain) {
-    const char* fn = "w4_chain_create";
-    if (!chain) return fail(W4_ERR_ARG, "%s: chain must not be NULL", fn);
-    *chain = nullptr;
-    if (!descs || !workspace) return fail(W4_ERR_NULL, "%s: descs and workspace must not be NULL", fn);
-    if (count <= 0) return fail(W4_ERR_ARG, "%s: count = %d must be positive", fn, count);
-    if (!aligned(workspace, 256)) return fail(W4_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
-    std::vector<Range> writes(count), reads(count), weights;
+// Host analysis of a chain: validation, stages, producers and the tagged
+// output copies (mirrors) the workspace must hold.
+struct ChainPlan {
     int num_stages = 0;
+    std::vector<int> producer;      // GEMV whose output is this GEMV's x, or -1
+    std::vector<long> mirror_word;  // word offset of this GEMV's mirror, or -1 (no reader)
+    size_t mirror_words = 0;
+};
+
+w4_status plan_chain(const char* fn, const w4_gemv_desc* descs, int count, ChainPlan& plan) {
+    if (!descs) return fail(W4_ERR_NULL, "%s: descs must not be NULL", fn);
+    if (count <= 0) return fail(W4_ERR_ARG, "%s: count = %d must be positive", fn, count);
+    std::vector<Range> writes(count), reads(count), weights;
     for (int i = 0; i < count; ++i) {
         const w4_gemv_desc& d = descs[i];
         if (!d.x || !d.y) return fail(W4_ERR_NULL, "%s: descriptor %d: x and y must not be NULL", fn, i);
@@ -231,7 +231,7 @@ W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* wor
         if (d.reserved != 0) return fail(W4_ERR_ARG, "%s: descriptor %d: reserved must be 0", fn, i);
         if (d.stage < 0 || (i > 0 && d.stage < descs[i - 1].stage))
             return fail(W4_ERR_ARG, "%s: descriptor %d: stages must be non-negative and non-decreasing", fn, i);
-        if (i == 0 || d.stage != descs[i - 1].stage) ++num_stages;
+        if (i == 0 || d.stage != descs[i - 1].stage) ++plan.num_stages;
         const size_t sz = (size_t)d.N * (d.K / W4_INT4_GROUP) * 2;
         writes[i] = range(d.y, (size_t)d.N * 2);
         reads[i] = range(d.x, (size_t)d.K * 2);
@@ -239,6 +239,9 @@ W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* wor
         weights.push_back(range(d.s, sz));
         weights.push_back(range(d.z, sz));
     }
+    if (plan.num_stages >= 65535) return fail(W4_ERR_ARG, "%s: %d stages (at most 65534)", fn, plan.num_stages);
+    plan.producer.assign(count, -1);
+    plan.mirror_word.assign(count, -1);
     for (int i = 0; i < count; ++i) {
         for (const Range& w : weights)
             if (overlap(writes[i], w)) return fail(W4_ERR_ALIAS, "%s: output %d overlaps a weight, scale or zero", fn, i);
@@ -247,15 +250,70 @@ W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* wor
             if (descs[j].stage == descs[i].stage && overlap(writes[i], reads[j]))
                 return fail(W4_ERR_ALIAS, "%s: output %d overlaps input %d of the same stage", fn, i, j);
         }
+        // An input written by an earlier GEMV must be exactly its output.
+        for (int j = 0; j < i; ++j) {
+            if (descs[j].stage == descs[i].stage || !overlap(writes[j], reads[i])) continue;
+            if (descs[i].x != descs[j].y || descs[i].K != descs[j].N)
+                return fail(W4_ERR_UNSUPPORTED, "%s: input %d overlaps output %d without being exactly that output",
+                            fn, i, j);
+            plan.producer[i] = j;
+        }
     }
-    const w4::ChainLayout lay = w4::chain_layout(count, num_stages);
+    // An output that overwrites an earlier GEMV's input must wait for that
+    // GEMV's output, through its chain of producers (a GEMV starts only once
+    // its producer's output is complete, and that output is computed after
+    // every workgroup has read the producer's input).
+    for (int j = 0; j < count; ++j)
+        for (int i = 0; i < count; ++i) {
+            if (descs[i].stage >= descs[j].stage || !overlap(writes[j], reads[i])) continue;
+            int p = plan.producer[j];
+            while (p >= 0 && p != i) p = plan.producer[p];
+            if (p != i)
+                return fail(W4_ERR_UNSUPPORTED,
+                            "%s: output %d overwrites input %d of an earlier stage without depending on its output",
+                            fn, j, i);
+        }
+    for (int i = 0; i < count; ++i) {
+        const int j = plan.producer[i];
+        if (j >= 0 && plan.mirror_word[j] < 0) {
+            plan.mirror_word[j] = (long)plan.mirror_words;
+            plan.mirror_words += ((size_t)descs[j].N + 63) / 64 * 64;
+        }
+    }
+    return W4_OK;
+}
+
+}  // namespace
+
+W4_API size_t w4_chain_workspace_bytes(const w4_gemv_desc* descs, int count) {
+    ChainPlan plan;
+    if (plan_chain("w4_chain_workspace_bytes", descs, count, plan) != W4_OK) return 0;
+    return w4::chain_layout(count, plan.num_stages, plan.mirror_words).total;
+}
+
+W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* workspace, size_t workspace_bytes,
+                                 w4_chain_t* chain) {
+    const char* fn = "w4_chain_create";
+    if (!chain) return fail(W4_ERR_ARG, "%s: chain must not be NULL", fn);
+    *chain = nullptr;
+    if (!descs || !workspace) return fail(W4_ERR_NULL, "%s: descs and workspace must not be NULL", fn);
+    if (!aligned(workspace, 256)) return fail(W4_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+    ChainPlan plan;
+    w4_status pst = plan_chain(fn, descs, count, plan);
+    if (pst != W4_OK) return pst;
+    const int num_stages = plan.num_stages;
+    const w4::ChainLayout lay = w4::chain_layout(count, num_stages, plan.mirror_words);
     if (workspace_bytes < lay.total)
         return fail(W4_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, lay.total, workspace_bytes);
-    for (int i = 0; i < count; ++i)
-        if (overlap(range(workspace, lay.total), writes[i]) || overlap(range(workspace, lay.total), reads[i]))
-            return fail(W4_ERR_ALIAS, "%s: workspace overlaps descriptor %d", fn, i);
-    for (const Range& w : weights)
-        if (overlap(range(workspace, lay.total), w)) return fail(W4_ERR_ALIAS, "%s: workspace overlaps a weight", fn);
+    for (int i = 0; i < count; ++i) {
+        const w4_gemv_desc& d = descs[i];
+        const Range ws = range(workspace, lay.total);
+        if (overlap(ws, range(d.y, (size_t)d.N * 2)) || overlap(ws, range(d.x, (size_t)d.K * 2)) ||
+            overlap(ws, range(d.qw, (size_t)d.N * d.K / 2)) ||
+            overlap(ws, range(d.s, (size_t)d.N * (d.K / W4_INT4_GROUP) * 2)) ||
+            overlap(ws, range(d.z, (size_t)d.N * (d.K / W4_INT4_GROUP) * 2)))
+            return fail(W4_ERR_ALIAS, "%s: workspace overlaps an operand of descriptor %d", fn, i);
+    }
 
     // Tables.
     std::vector<w4::ChainStage> stages;
@@ -264,7 +322,7 @@ W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* wor
     for (int i = 0; i < count; ++i) {
         const w4_gemv_desc& d = descs[i];
         if (i == 0 || d.stage != descs[i - 1].stage) {
-            stages.push_back({i, 0, 0, 0, 0});
+            stages.push_back({i, 0, 0, 0});
             x_bytes = 0;
         }
         w4::ChainStage& st = stages.back();
@@ -279,9 +337,7 @@ W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* wor
         g.sp = g.C <= 128 ? 1 : (g.C <= 256 ? 2 : 4);
         g.tile0 = st.tiles;
         g.x_lds = x_bytes;
-        g.x_internal = 0;
-        for (int j = 0; j < i && !g.x_internal; ++j)
-            if (descs[j].stage < d.stage && overlap(writes[j], reads[i])) g.x_internal = 1;
+        g.x_internal = plan.producer[i] >= 0;
         st.x_internal |= g.x_internal;
         x_bytes += w4::chain_x_lds_bytes(g.C);
         if (x_bytes > w4::kChainXLdsBytes)
@@ -291,8 +347,22 @@ W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* wor
         st.tiles += (d.N + rows_per_tile - 1) / rows_per_tile;
         st.ngemv += 1;
     }
-    for (size_t t = 1; t < stages.size(); ++t)
-        stages[t].internal_through = stages[t - 1].internal_through + stages[t].x_internal;
+    char* base = static_cast<char*>(workspace);
+    unsigned* mirrors = reinterpret_cast<unsigned*>(base + lay.mirrors);
+    for (int i = 0; i < count; ++i) {
+        gemvs[i].ym = plan.mirror_word[i] >= 0 ? mirrors + plan.mirror_word[i] : nullptr;
+        gemvs[i].xm = plan.producer[i] >= 0 ? mirrors + plan.mirror_word[plan.producer[i]] : nullptr;
+        gemvs[i].xm_stage = 0;
+        gemvs[i].reserved = 0;
+    }
+    for (int t = 0; t < num_stages; ++t)
+        for (int k = 0; k < stages[t].ngemv; ++k) {
+            const int i = stages[t].gemv0 + k;
+            if (plan.producer[i] < 0) continue;
+            const int j = plan.producer[i];
+            for (int u = 0; u < num_stages; ++u)
+                if (j >= stages[u].gemv0 && j < stages[u].gemv0 + stages[u].ngemv) gemvs[i].xm_stage = u;
+        }
     int occ = 0, cus = 0, dev = 0;
     hipError_t err = w4::chain_occupancy(&occ);
     if (err == hipSuccess) err = hipGetDevice(&dev);
@@ -302,8 +372,9 @@ W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* wor
     int workers = cus;  // one workgroup per compute unit, all resident at once
     if (workers > w4::kChainMaxWorkers) workers = w4::kChainMaxWorkers;
 
-    char* base = static_cast<char*>(workspace);
+    // Zero the counters and the mirrors (tag 0 is never a valid tag).
     err = hipMemset(base, 0, lay.stages);
+    if (err == hipSuccess && plan.mirror_words) err = hipMemset(base + lay.mirrors, 0, plan.mirror_words * 4);
     if (err == hipSuccess)
         err = hipMemcpy(base + lay.stages, stages.data(), stages.size() * sizeof(w4::ChainStage), hipMemcpyHostToDevice);
     if (err == hipSuccess)
@@ -315,8 +386,7 @@ W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* wor
     L.stages = reinterpret_cast<const w4::ChainStage*>(base + lay.stages);
     L.gemvs = reinterpret_cast<const w4::ChainGemv*>(base + lay.gemvs);
     L.err = reinterpret_cast<unsigned*>(base + lay.err);
-    L.flags = reinterpret_cast<unsigned*>(base + lay.flags);
-    L.go = reinterpret_cast<unsigned*>(base + lay.go);
+    L.counters = reinterpret_cast<unsigned*>(base + lay.counters);
     L.num_stages = num_stages;
     L.workers = workers;
     L.spin_limit = 1u << 20;

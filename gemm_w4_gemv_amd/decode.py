@@ -49,8 +49,7 @@ class DecodeStep:
         self.graph: W4Graph | None = None
         self.chain = None
         if mode == "chain":
-            stages = [lin["stage"] for lin in self.linears]
-            nbytes = w4_chain_workspace_bytes(len(stages), len(set(stages)))
+            nbytes = w4_chain_workspace_bytes(self.linears)
             self.workspace = torch.zeros(nbytes + 256, dtype=torch.uint8, device="cuda")
             off = (-self.workspace.data_ptr()) % 256
             self.chain = w4_chain_create(self.linears, self.workspace[off:off + nbytes])

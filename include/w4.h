@@ -174,31 +174,40 @@ W4_API void w4_graph_destroy(w4_graph_t graph);
  *
  * Each descriptor is one w4_gemv (same operands, layouts and limits, plus
  * K <= W4_CHAIN_MAX_K) tagged with a stage number.  Descriptors must be given
- * in non-decreasing stage order.  GEMVs of one stage may run in any order or
- * concurrently; every GEMV of a later stage starts after every GEMV of the
- * earlier stages has written its output, so a later stage may read (as x)
- * what an earlier stage wrote (as y).  An output must not overlap any
- * weight, scale or zero of the chain, any other output, or any input of its
- * own stage.  The x vectors of one stage must fit the kernel's LDS staging
- * area: the sum over the stage's GEMVs of 68 * ceil(K / 4096) * 128 bytes
- * at most 65536 (W4_ERR_SHAPE otherwise).
+ * in non-decreasing stage order.  The result is that of running the stages
+ * one after another, each stage's GEMVs in any order: a GEMV may read as x
+ * the output y of a GEMV of an earlier stage, and then sees it complete.
+ * Such an input must be exactly that output (same pointer, K equal to the
+ * producer's N); a partial overlap is W4_ERR_UNSUPPORTED.  Inside the launch
+ * a GEMV waits only for the output it reads (its readers poll a tagged copy
+ * of it, kept in the workspace), so GEMVs that do not depend on each other
+ * may overlap in time.  Hence an output may overwrite an earlier stage's
+ * input only if its GEMV depends, through its chain of inputs, on that
+ * earlier GEMV's output (W4_ERR_UNSUPPORTED otherwise).  An output must not
+ * overlap any weight, scale or zero of the chain, any other output, or any
+ * input of its own stage (W4_ERR_ALIAS).  The x vectors of one stage must
+ * fit the kernel's LDS staging area: the sum over the stage's GEMVs of
+ * 68 * ceil(K / 4096) * 128 bytes at most 65536 (W4_ERR_SHAPE otherwise).
+ * At most 65534 stages.
  *
- * w4_chain_create validates the descriptors on the host, then (blocking, not
- * capturable) zeroes the synchronisation words of ``workspace`` and writes
- * the chain's tables into it; it never allocates device memory.  The
- * workspace (device memory, 256-byte aligned, at least
- * w4_chain_workspace_bytes(count, count) bytes) belongs to the chain until
+ * w4_chain_workspace_bytes(descs, count) validates the descriptors and
+ * returns the workspace size they need (0 if they are invalid; the reason
+ * is in w4_last_error).  w4_chain_create validates the descriptors on the
+ * host, then (blocking, not capturable) clears the workspace's counters and
+ * tagged copies and writes the chain's tables into it; it never allocates
+ * device memory.  The workspace (device memory, 256-byte aligned, at least
+ * w4_chain_workspace_bytes(descs, count) bytes) belongs to the chain until
  * w4_chain_destroy.  w4_chain_run enqueues one run on ``stream`` (one kernel
  * launch; capturable into a graph).  Runs of one chain must not overlap each
  * other or any other kernel that fills the GPU: the launch keeps one
- * workgroup resident on every compute unit and they wait for each other.  Every
- * wait is bounded: a run that cannot make progress ends within about a
+ * workgroup resident on every compute unit and they wait for each other.
+ * Every wait is bounded: a run that cannot make progress ends within about a
  * second and records a non-zero error word; w4_chain_error synchronises the
  * device and returns that word (0 = no error).  After a non-zero error word,
  * create the chain again before running it.
  * Errors: W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_UNSUPPORTED, W4_ERR_ALIGN,
- * W4_ERR_ALIAS, W4_ERR_ARG (no descriptors, stage order), W4_ERR_WORKSPACE,
- * W4_ERR_HIP.
+ * W4_ERR_ALIAS, W4_ERR_ARG (no descriptors, stage order, too many stages),
+ * W4_ERR_WORKSPACE, W4_ERR_HIP.
  */
 #define W4_CHAIN_MAX_K 16384
 
@@ -215,7 +224,7 @@ typedef struct w4_gemv_desc {
 } w4_gemv_desc;
 
 typedef struct w4_chain* w4_chain_t;
-W4_API size_t w4_chain_workspace_bytes(int count, int num_stages);
+W4_API size_t w4_chain_workspace_bytes(const w4_gemv_desc* descs, int count);
 W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* workspace,
                                  size_t workspace_bytes, w4_chain_t* chain);
 W4_API w4_status w4_chain_run(w4_chain_t chain, void* stream);

@@ -159,8 +159,19 @@ def test_chain_validation():
         assert h.value is None
         return st
 
-    assert lib.w4_chain_workspace_bytes(336, 192) > 128 * 1024
-    assert lib.w4_chain_workspace_bytes(0, 1) == 0
+    def ws_bytes(descs):
+        arr = (w4.GemvDesc * max(len(descs), 1))(*descs)
+        return lib.w4_chain_workspace_bytes(ctypes.cast(arr, ctypes.c_void_p), len(descs))
+
+    one = ws_bytes([desc()])
+    assert one > 128 * 1024
+    assert ws_bytes([]) == 0
+    assert ws_bytes([desc(K=100)]) == 0                        # invalid descriptors
+    # q (stage 0) -> o (stage 1) reading q's output exactly: the workspace
+    # also holds the tagged copy of q's 4096 outputs
+    q = desc(K=3840, N=4096, y=Y)
+    o = desc(x=Y, K=4096, N=3840, y=Y + 65536, stage=1)
+    assert ws_bytes([q, o]) >= ws_bytes([q, desc(N=3840, y=Y + 65536, stage=1)]) + 4096 * 4
     assert create([desc()], ws=None) == NULL
     assert create([desc(K=16384 + 128)]) == SHAPE          # the chain's K limit
     assert create([desc(K=100)]) == SHAPE
@@ -173,6 +184,16 @@ def test_chain_validation():
     assert create([desc(y=QW + 64)]) == ALIAS                 # output over a weight
     assert create([desc(), desc(x=Y, y=Y + 65536)]) == ALIAS  # same-stage read of an output
     assert create([desc()], nbytes=64) == WS
+    # an input written by an earlier stage must be exactly that output
+    assert create([desc(N=4096, y=Y), desc(x=Y + 64, K=3840, N=3840, y=Y + 65536, stage=1)]) == UNSUP
+    assert create([desc(N=4096, y=Y), desc(x=Y, K=3840, N=3840, y=Y + 65536, stage=1)]) == UNSUP  # K != N
+    # a later output over an earlier input needs a path of inputs back to that GEMV's output
+    a0 = desc(x=X, K=3840, N=3840, y=Y, stage=0)
+    b1 = desc(x=Y + 65536, K=3840, N=3840, y=X, stage=1)      # overwrites a0's input, does not read a0's output
+    assert create([a0, b1]) == UNSUP
+    assert ws_bytes([a0, b1]) == 0
+    c1 = desc(x=Y, K=3840, N=3840, y=X, stage=1)              # reads a0's output: allowed
+    assert ws_bytes([a0, c1]) > 0
     h = ctypes.c_void_p()
     assert lib.w4_chain_create(None, 1, WSP, 1 << 20, ctypes.byref(h)) == NULL
     assert lib.w4_chain_create((w4.GemvDesc * 1)(desc()), 0, WSP, 1 << 20, ctypes.byref(h)) == ARG
