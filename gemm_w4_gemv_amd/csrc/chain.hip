@@ -448,41 +448,44 @@ __device__ void compute_wave(const ChainLaunch& L, Shared& sh, const unsigned ch
 
     if (a.s >= L.num_stages) return;
 
-    // One tile in flight per wave: compute it, store its rows, then issue the
-    // next tile's loads, which are then on their way while the next stage's
-    // inputs arrive.  A tile two or more stages ahead is not issued until the
-    // stage before it is staged: weights then reach the memory system in
-    // stage order, and a stage's tiles do not queue behind later stages'.
-    // Nothing but the tile in R is in flight at the loop head, so the
-    // compiler's waits there are exact.  No wave ever waits for its own
-    // stores: readers poll the tagged outputs.
-    TileRegs R;
-    ChainGemv Ga = L.gemvs[a.g];
-    issue(Ga, a, false, lane, R);
-    for (;;) {
-        // The next work and its table entries first: their scalar loads are
-        // then in flight during this tile's math, not after it.
-        const Work b = advance(L, a, v, W);
-        const bool has_b = b.s < L.num_stages;
-        const bool near = has_b && b.s <= a.s + 1;
-        const ChainGemv Gb = L.gemvs[has_b ? b.g : a.g];
-        if (x_stage != a.s) {
-            wait_x(a.s);
-            x_stage = a.s;
+    // Two tiles in flight per wave, in two register sets used in turn: while
+    // one tile is computed the next one loads, and after the math the set is
+    // refilled with the tile after next.  Past the wave's last tile the refill
+    // is a dummy (an empty buffer range, which returns zeros without touching
+    // memory), so every step issues the same loads and the compiler's wait
+    // before a tile's math covers exactly that tile.  No wave ever waits for
+    // its own stores: readers poll the tagged outputs.
+    TileRegs R0, R1;
+    Work cur = a;
+    Work nxt = advance(L, cur, v, W);
+    ChainGemv Gc = L.gemvs[cur.g];
+    ChainGemv Gn = L.gemvs[nxt.s < L.num_stages ? nxt.g : cur.g];
+    issue(Gc, cur, false, lane, R0);
+    issue(Gn, nxt.s < L.num_stages ? nxt : cur, nxt.s >= L.num_stages, lane, R1);
+    // Compute cur from Rc (nxt is loading in the other set); refill Rc with
+    // the tile after nxt.  False once cur was the wave's last tile.
+    auto step = [&](TileRegs& Rc) -> bool {
+        const bool has_n = nxt.s < L.num_stages;
+        const Work n2 = has_n ? advance(L, nxt, v, W) : nxt;
+        const bool has_n2 = n2.s < L.num_stages;
+        const ChainGemv G2 = L.gemvs[has_n2 ? n2.g : cur.g];
+        if (x_stage != cur.s) {
+            wait_x(cur.s);
+            x_stage = cur.s;
         }
-        compute(Ga, a, lane, R, xl + (size_t)(a.s & 1) * kChainXLdsBytes + Ga.x_lds, stage_tag(sh, a.s));
-        // Keep the next tile's loads below this tile's stores.
+        compute(Gc, cur, lane, Rc, xl + (size_t)(cur.s & 1) * kChainXLdsBytes + Gc.x_lds, stage_tag(sh, cur.s));
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("" ::: "memory");
-        if (near) issue(Gb, b, false, lane, R);
-        if (b.s != a.s) report(b.s);
-        if (!has_b) break;
-        if (!near) {
-            wait_x(b.s - 1);
-            issue(Gb, b, false, lane, R);
-        }
-        a = b;
-        Ga = Gb;
+        issue(G2, has_n2 ? n2 : cur, !has_n2, lane, Rc);
+        if (nxt.s != cur.s) report(nxt.s);  // cur was this wave's last tile of its stage
+        if (!has_n) return false;
+        cur = nxt;
+        Gc = Gn;
+        nxt = n2;
+        Gn = G2;
+        return true;
+    };
+    while (step(R0) && step(R1)) {
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
