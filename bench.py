@@ -4,17 +4,23 @@
 The timed step is one replay of the decode step's HIP graph: 48 layers x 7
 INT4 linears (q 3840->4096, k and v 3840->2048, o 4096->3840, gate and up
 3840->15360, down 15360->3840), group 128, FP16 scale and zero, BF16
-activations, M = 1, every linear reading its own static input.  The graph
-holds one launch of the persistent decode-chain kernel, which runs the 336
-GEMVs with the decoder's dependencies as stages ({q,k,v} -> {o} ->
-{gate,up} -> {down} per layer).  Inputs are seeded synthetic data already
-resident in device memory.  ``value`` is the algorithmic bytes of one step
-(packed weights + scales + zeros + x + y, each once) divided by the
-measured time per step.
+activations, M = 1, each linear reading the output it reads in a decoder:
+layer 0's q, k and v read one seeded N(0,1) input; o reads q's output, gate
+and up read o's, down reads gate's, and the next layer's q, k and v read
+down's (attention and the gate/up product are outside this path).  Values
+grow about 1000x per layer and overflow BF16 after about a dozen layers;
+no kernel's timing depends on the values.  The graph holds one launch of
+the persistent decode-chain kernel, in which each GEMV waits for exactly
+the output it reads.  Inputs are seeded synthetic data already resident in
+device memory.  ``value`` is the algorithmic bytes of one step (packed
+weights + scales + zeros + x + y, each once) divided by the measured time
+per step.
 
 Also reported, outside the timed step:
   * ``roofline``: the chain kernel's own achieved bandwidth, from HIP events
     around each of its launches on the stream it runs on;
+  * ``extra.decode_step_independent_inputs``: the same linears, each reading
+    its own N(0,1) input (no GEMV waits for another), in one chain launch;
   * ``extra.decode_step_336_launch_graph``: the same step as a graph of 336
     separate w4_gemv launches, with per-shape kernel timings;
   * ``extra``: the single 3840 x 3840 GEMV, the 262144-row logits GEMV, the
@@ -26,7 +32,7 @@ Also reported, outside the timed step:
     python bench.py [--steps K] [--warmup W] [--no-extra] [--no-cpu-baseline]
     python bench.py --counters   # only the kernels that HBM counters are read for
 
-``--counters`` runs five chain-kernel launches of the decode step, then five
+``--counters`` runs five chain-kernel launches of the (timed, linked) decode step, then five
 copies of 512 MiB by torch (a plain copy of known size, read once and
 written once), for ``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE``
 runs.  The counters' per-launch figures for the chain kernel, scaled by
@@ -95,6 +101,7 @@ def measured_traffic():
 
 # ------------------------------------------------------------------ helpers
 def decode_linears(host, si, torch):
+    """The 336 linears of the decode step, each reading its own seeded N(0,1) input."""
     from gemm_w4_gemv_amd.decode import LAYER_STAGE
 
     lins = []
@@ -102,12 +109,23 @@ def decode_linears(host, si, torch):
         lin_np, x_bits = si.decode_linear(layer, idx)
         t = host.int4_tensors(lin_np)
         t["x"] = host.bf16_tensor(x_bits)
-        t["y"] = torch.empty(N, dtype=torch.bfloat16, device="cuda")
-        t["name"], t["K"], t["N"] = name, K, N
+        t["y"] = torch.zeros(N, dtype=torch.bfloat16, device="cuda")
+        t["name"], t["layer"], t["K"], t["N"] = name, layer, K, N
         t["stage"] = 4 * layer + LAYER_STAGE[name]
         lins.append(t)
     torch.cuda.synchronize()
     return lins
+
+
+def linked_copy(lins):
+    """The same linears (same weights and output buffers), each reading the
+    output it reads in a decoder; layer 0's q, k and v read q's input."""
+    from gemm_w4_gemv_amd.decode import link_decoder_inputs
+    out = [dict(t) for t in lins]
+    for t in out[1:3]:
+        t["x"] = out[0]["x"]
+    link_decoder_inputs(out)
+    return out
 
 
 def time_graph(torch, replay, stream, reps: int, warmup: int = 2):
@@ -265,7 +283,7 @@ def cpu_baseline(si, rf, layers: int):
 def counter_run(torch, host, si) -> int:
     """Five chain launches of the decode step, then five 512 MiB torch copies."""
     from gemm_w4_gemv_amd.decode import DecodeStep
-    lins = decode_linears(host, si, torch)
+    lins = linked_copy(decode_linears(host, si, torch))
     step = DecodeStep(lins, mode="chain")
     torch.cuda.synchronize()
     for _ in range(5):
@@ -313,7 +331,8 @@ def main() -> int:
         return counter_run(torch, host, si)
 
     log("generating and uploading the decode step (336 INT4 linears)")
-    lins = decode_linears(host, si, torch)
+    own = decode_linears(host, si, torch)
+    lins = linked_copy(own)
     step_bytes = sum(rf.int4_linear_bytes(l["K"], l["N"]) for l in lins)
     step_flops = sum(rf.flops(1, l["K"], l["N"]) for l in lins)
     step = DecodeStep(lins, mode="chain")
@@ -356,13 +375,26 @@ def main() -> int:
     achieved = step_bytes / (avg_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / rf.HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
-                "kernel": "chain_kernel (336 INT4 GEMVs, 192 stages, one launch per decode step)",
+                "kernel": "chain_kernel (336 INT4 GEMVs in 192 stages, each waiting for the output it reads; "
+                          "one launch per decode step)",
                 "bytes_per_launch": step_bytes, "avg_launch_us": round(avg_us, 2), "launches_timed": reps}
     log(f"chain kernel: {avg_us:.1f} us/launch, {achieved:.0f} GB/s")
     step.destroy()
 
-    # the same step as 336 separate launches
+    # the same linears each reading its own input: no GEMV waits for another
     extra = {}
+    step3 = DecodeStep(own, mode="chain")
+    step3.capture()
+    ms3 = time_graph(torch, step3.replay, step3.stream, reps=args.steps, warmup=args.warmup)
+    err3 = step3.chain.error()
+    extra["decode_step_independent_inputs"] = {
+        "us_per_step": round(ms3 * 1e3, 1), "GBps": round(step_bytes / (ms3 * 1e-3) / 1e9, 1),
+        "note": "same 336 linears, each reading its own N(0,1) input, so no GEMV waits for another "
+                "(weight streaming with no dependencies, not a decode step)", "error_word": err3}
+    log(f"336 GEMVs with independent inputs (chain): {ms3 * 1e3:.1f} us")
+    step3.destroy()
+
+    # the same step as 336 separate launches
     step2 = DecodeStep(lins, mode="launches")
     step2.capture()
     ms2 = time_graph(torch, step2.replay, step2.stream, reps=args.steps, warmup=args.warmup)
@@ -398,8 +430,9 @@ def main() -> int:
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "decode step: one hipGraph replay of 48 layers x 7 INT4 GEMVs "
-                               "(q,k,v,o,gate,up,down; hidden 3840; group 128; M=1) run by the persistent "
-                               "chain kernel with stages {q,k,v}->{o}->{gate,up}->{down} per layer",
+                               "(q,k,v,o,gate,up,down; hidden 3840; group 128; M=1), each reading the output "
+                               "it reads in a decoder (o<-q, gate/up<-o, down<-gate, next q/k/v<-down), "
+                               "run by the persistent chain kernel",
                    "linears": n_lins, "stages": 192, "bytes_per_step": step_bytes, "flops_per_step": step_flops,
                    "us_per_step": round(ms_per_step * 1e3, 1), "gpu_us_per_step": round(gpu_ms_per_step * 1e3, 1),
                    "frac_hbm": round(value / rf.HBM_PEAK_GBPS, 4)},

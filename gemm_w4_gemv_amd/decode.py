@@ -4,9 +4,10 @@ Two ways to run the step are offered:
 
 * ``launches``: one ``w4_gemv`` launch per linear (336 graph nodes);
 * ``chain``: one ``w4_chain_run`` launch (a single graph node) of the
-  persistent chain kernel, with the decoder's dependencies as stages:
-  per layer {q, k, v} -> {o} -> {gate, up} -> {down}, each stage starting
-  after the previous one has written its outputs.
+  persistent chain kernel, with the decoder's linears as stages: per layer
+  {q, k, v} -> {o} -> {gate, up} -> {down}.  A linear whose input is another
+  linear's output (see ``link_decoder_inputs``) waits for exactly that
+  output.
 
 "Lab 5: Gemma4 端到端推理优化", section "CUDA Graph": after the fused GEMV the
 remaining cost was launch and Python overhead, so the whole decode step is
@@ -27,9 +28,36 @@ from . import w4_gemv, w4_graph_begin, w4_graph_end, W4Graph, w4_chain_create, w
 LAYER_STAGE = {"q": 0, "k": 0, "v": 0, "o": 1, "gate": 2, "up": 2, "down": 3}
 
 
+# the output each decoder linear reads: "h" is the layer's input (the first
+# layer's own input; for later layers the previous layer's down output)
+DECODER_INPUT = {"q": "h", "k": "h", "v": "h", "o": "q", "gate": "o", "up": "o", "down": "gate"}
+
+
 def decoder_stages(names, layers_of):
     """Stage number of every linear, from its name and layer index."""
     return [4 * layer + LAYER_STAGE[name] for name, layer in zip(names, layers_of)]
+
+
+def link_decoder_inputs(linears) -> None:
+    """Make every linear read the output it reads in a decoder layer.
+
+    ``linears`` are dicts with ``name``, ``layer``, ``x`` and ``y``, in layer
+    order.  The first layer's q, k and v keep their own ``x`` (they must share
+    one buffer); every other input becomes the producing linear's ``y``: o
+    reads q's output, gate and up read o's, down reads gate's (the gate/up
+    product and the attention between q and o are outside this path), and a
+    layer's q, k and v read the previous layer's down output.
+    """
+    out = {}
+    for lin in linears:
+        layer, name = lin["layer"], lin["name"]
+        src = DECODER_INPUT[name]
+        if src == "h":
+            if layer > 0:
+                lin["x"] = out[(layer - 1, "down")]
+        else:
+            lin["x"] = out[(layer, src)]
+        out[(layer, name)] = lin["y"]
 
 
 class DecodeStep:

@@ -406,6 +406,59 @@ def test_chain_data_dependent():
     step.destroy()
 
 
+def test_chain_two_decoder_layers():
+    """Two full decoder layers wired as a decoder reads them, as the timed decode step is.
+
+    q, k and v of layer 0 read one input; o reads q's output, gate and up
+    read o's, down reads gate's, layer 1's q, k and v read layer 0's down
+    output.  GEMVs that do not depend on each other may overlap in the
+    kernel; every one of the 14 outputs is compared in full with the oracle
+    run in the same order (each intermediate rounded to BF16 as stored).
+    The outputs are zeroed before every replay, and the tagged copies keep
+    the previous replay's values, so a reader that took a stale copy fails.
+    """
+    from gemm_w4_gemv_amd.decode import LAYER_STAGE, link_decoder_inputs
+    shapes = {n: (K, N) for n, K, N in si.DECODE_LAYER}
+    x0_bits = si.bf16_normal(9, (0,), (3840,))
+    h0 = host.bf16_tensor(x0_bits)
+    gemvs, lin_nps = [], []
+    for layer in range(2):
+        for idx, (name, K, N) in enumerate(si.DECODE_LAYER):
+            lin_np = si.int4_linear(9, (1, layer, idx), K, N)
+            t = host.int4_tensors(lin_np)
+            t["x"] = h0
+            t["y"] = torch.zeros(N, dtype=torch.bfloat16, device=DEV)
+            t["name"], t["layer"], t["stage"] = name, layer, 4 * layer + LAYER_STAGE[name]
+            gemvs.append(t)
+            lin_nps.append(lin_np)
+    link_decoder_inputs(gemvs)
+    # oracle in layer order with the same wiring
+    outs, refs = {}, []
+    for t, lin_np in zip(gemvs, lin_nps):
+        src = {"q": "h", "k": "h", "v": "h", "o": "q", "gate": "o", "up": "o", "down": "gate"}[t["name"]]
+        if src == "h":
+            xb = x0_bits if t["layer"] == 0 else outs[(t["layer"] - 1, "down")]
+        else:
+            xb = outs[(t["layer"], src)]
+        assert xb.shape[0] == shapes[t["name"]][0]
+        y_ref, wmax = int4_ref(lin_np, xb)
+        refs.append((y_ref[0], wmax, xnorm(xb)))
+        outs[(t["layer"], t["name"])] = oracle.bf16_bits(y_ref[0])
+    step = DecodeStep(gemvs, mode="chain")
+    step.capture()
+    for rep in range(3):
+        for t in gemvs:
+            t["y"].zero_()
+        torch.cuda.synchronize()
+        step.replay()
+        step.stream.synchronize()
+        for t, (y_ref, wmax, xn) in zip(gemvs, refs):
+            check_outputs(host.bf16_values(t["y"]), y_ref, xn, wmax,
+                          f"layer {t['layer']} {t['name']} replay {rep}")
+    assert step.chain.error() == 0
+    step.destroy()
+
+
 def test_chain_mixed_shapes():
     """Stages mixing K classes (one, two and four waves per row), ragged N and tiny stages."""
     plan = [[(128, 1), (1024, 7)], [(8192, 100)], [(4096, 1000), (15360, 3), (256, 33)], [(16384, 9)],
