@@ -258,7 +258,7 @@ __device__ __forceinline__ void compute(const ChainGemv& G, const Work& w, int l
 // (slots cover each GEMV's padded chunk count).
 __device__ __forceinline__ bool stage_slot(const ChainLaunch& L, const ChainStage& st, int k, int& g, int& m) {
     for (int gi = 0; gi < st.ngemv; ++gi) {
-        const int n = chain_x_chunks(L.gemvs[st.gemv0 + gi].C) / kWave;
+        const int n = L.gemvs[st.gemv0 + gi].x_slots;
         if (k < n) {
             g = uniform(st.gemv0 + gi);
             m = uniform(k);
@@ -271,7 +271,7 @@ __device__ __forceinline__ bool stage_slot(const ChainLaunch& L, const ChainStag
 
 __device__ __forceinline__ int stage_slots(const ChainLaunch& L, const ChainStage& st) {
     int n = 0;
-    for (int gi = 0; gi < st.ngemv; ++gi) n += chain_x_chunks(L.gemvs[st.gemv0 + gi].C) / kWave;
+    for (int gi = 0; gi < st.ngemv; ++gi) n += L.gemvs[st.gemv0 + gi].x_slots;
     return n;
 }
 

@@ -29,7 +29,7 @@ struct ChainGemv {
     unsigned* ym;
     const unsigned* xm;
     int xm_stage;  // stage index of xm's writer (its tags)
-    int reserved;
+    int x_slots;   // 64-chunk staging slots of x; 0 when an earlier GEMV of the stage has the same x
 };
 
 // GEMVs gemv0 .. gemv0 + ngemv - 1 form one stage: they run concurrently;

@@ -336,10 +336,20 @@ W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* wor
         g.N = d.N;
         g.sp = g.C <= 128 ? 1 : (g.C <= 256 ? 2 : 4);
         g.tile0 = st.tiles;
-        g.x_lds = x_bytes;
         g.x_internal = plan.producer[i] >= 0;
         st.x_internal |= g.x_internal;
-        x_bytes += w4::chain_x_lds_bytes(g.C);
+        // GEMVs of a stage with the same input share one staged copy.
+        int same = -1;
+        for (int j = st.gemv0; j < i && same < 0; ++j)
+            if (descs[j].x == d.x && descs[j].K == d.K) same = j;
+        if (same >= 0) {
+            g.x_lds = gemvs[same].x_lds;
+            g.x_slots = 0;
+        } else {
+            g.x_lds = x_bytes;
+            g.x_slots = w4::chain_x_chunks(g.C) / 64;
+            x_bytes += w4::chain_x_lds_bytes(g.C);
+        }
         if (x_bytes > w4::kChainXLdsBytes)
             return fail(W4_ERR_SHAPE, "%s: the inputs of stage %d need %d bytes of LDS (limit %d)",
                         fn, d.stage, x_bytes, w4::kChainXLdsBytes);
@@ -353,7 +363,6 @@ W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* wor
         gemvs[i].ym = plan.mirror_word[i] >= 0 ? mirrors + plan.mirror_word[i] : nullptr;
         gemvs[i].xm = plan.producer[i] >= 0 ? mirrors + plan.mirror_word[plan.producer[i]] : nullptr;
         gemvs[i].xm_stage = 0;
-        gemvs[i].reserved = 0;
     }
     for (int t = 0; t < num_stages; ++t)
         for (int k = 0; k < stages[t].ngemv; ++k) {
