@@ -25,10 +25,7 @@ Also reported, outside the timed step:
     separate w4_gemv launches, with per-shape kernel timings;
   * ``extra``: the single 3840 x 3840 GEMV, the 262144-row logits GEMV, the
     two M = 128 prefill GEMMs (TFLOP/s) and the six-expert FP4 MoE pair,
-    each replayed as a graph over rotated weight copies so the data comes
-    from HBM; the two GEMVs also as back-to-back launches on a stream
-    (``eager_*``: on MI355X a graph adds several microseconds per node to
-    these short kernels);
+    each replayed over rotated weight copies so the data comes from HBM;
   * ``cpu_baseline``: the FP64 oracle timed on host cores on a sample of the
     same step.
 
@@ -131,21 +128,6 @@ def linked_copy(lins):
     return out
 
 
-def eager_us(torch, stream, call, copies, rounds: int = 10) -> float:
-    """Microseconds per call of back-to-back launches over ``copies`` (HIP events on ``stream``)."""
-    for t in copies:
-        call(t)
-    stream.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(rounds):
-        for t in copies:
-            call(t)
-    b.record(stream)
-    b.synchronize()
-    return a.elapsed_time(b) * 1e3 / (rounds * len(copies))
-
-
 def time_graph(torch, replay, stream, reps: int, warmup: int = 2):
     """Milliseconds per replay, from HIP events on ``stream`` around ``reps`` replays."""
     for _ in range(warmup):
@@ -203,15 +185,12 @@ def extra_workloads(w4, host, si, torch, rf):
     g = capture(w4, torch, stream, lambda: [w4.w4_gemv(x, t["qw"], t["s"], t["z"], y, stream=stream) for t in copies])
     ms = time_graph(torch, lambda: g.replay(stream), stream, reps=20)
     us = ms * 1e3 / n_copies
-    us_eager = eager_us(torch, stream, lambda t: w4.w4_gemv(x, t["qw"], t["s"], t["z"], y, stream=stream), copies)
     gbps = rf.int4_linear_bytes(K, N) / (us * 1e-6) / 1e9
     out["single_gemv_3840x3840"] = {"us_per_call": round(us, 3), "GBps": round(gbps, 1),
-                                    "frac_hbm": round(gbps / rf.HBM_PEAK_GBPS, 4), "copies": n_copies,
-                                    "eager_us_per_call": round(us_eager, 3),
-                                    "eager_GBps": round(rf.int4_linear_bytes(K, N) / (us_eager * 1e-6) / 1e9, 1)}
+                                    "frac_hbm": round(gbps / rf.HBM_PEAK_GBPS, 4), "copies": n_copies}
     g.destroy()
     del copies
-    log(f"single GEMV 3840x3840: {us:.2f} us, {gbps:.0f} GB/s (eager launches: {us_eager:.2f} us)")
+    log(f"single GEMV 3840x3840: {us:.2f} us, {gbps:.0f} GB/s")
 
     # logits GEMV 3840 -> 262144
     K, N = si.LOGITS_SHAPE
@@ -221,16 +200,12 @@ def extra_workloads(w4, host, si, torch, rf):
     g = capture(w4, torch, stream, lambda: [w4.w4_gemv(x, t["qw"], t["s"], t["z"], y, stream=stream) for t in copies])
     ms = time_graph(torch, lambda: g.replay(stream), stream, reps=20)
     us = ms * 1e3 / 2
-    us_eager = eager_us(torch, stream, lambda t: w4.w4_gemv(x, t["qw"], t["s"], t["z"], y, stream=stream), copies)
     gbps = rf.int4_linear_bytes(K, N) / (us * 1e-6) / 1e9
-    gbps_eager = rf.int4_linear_bytes(K, N) / (us_eager * 1e-6) / 1e9
     out["logits_gemv_3840x262144"] = {"us_per_call": round(us, 2), "GBps": round(gbps, 1),
-                                      "frac_hbm": round(gbps / rf.HBM_PEAK_GBPS, 4),
-                                      "eager_us_per_call": round(us_eager, 2), "eager_GBps": round(gbps_eager, 1),
-                                      "eager_frac_hbm": round(gbps_eager / rf.HBM_PEAK_GBPS, 4)}
+                                      "frac_hbm": round(gbps / rf.HBM_PEAK_GBPS, 4)}
     g.destroy()
     del copies
-    log(f"logits GEMV: {us:.1f} us, {gbps:.0f} GB/s (eager launches: {us_eager:.1f} us, {gbps_eager:.0f} GB/s)")
+    log(f"logits GEMV: {us:.1f} us, {gbps:.0f} GB/s")
 
     # prefill M = 128
     M = si.PREFILL_M

@@ -27,7 +27,7 @@
 #include "w4_internal.hpp"
 
 #ifndef W4_GEMV_MIN_BLOCKS
-#define W4_GEMV_MIN_BLOCKS 4096  // launch at least this many workgroups when N allows
+#define W4_GEMV_MIN_BLOCKS 1024  // launch at least this many workgroups when N allows
 #endif
 
 namespace w4 {
