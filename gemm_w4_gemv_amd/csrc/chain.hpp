@@ -50,9 +50,9 @@ constexpr int kChainLineWords = 32;    // one 128-byte line per launch counter
 constexpr int kChainMaxC = 512;        // K <= 16384
 constexpr int kChainXLdsBytes = 65536; // staged x (pairs + chunk sums) of one stage; two buffers
 
-// Staged x of one GEMV is zero-padded to whole segments of 128 chunks, so
-// the kernel never masks a chunk index.
-__host__ __device__ inline int chain_x_chunks(int C) { return (C + 127) / 128 * 128; }
+// Staged x of one GEMV is zero-padded to the sp segments of 128 chunks its
+// tiles read (128, 256 or 512 chunks), so the kernel never masks a chunk index.
+__host__ __device__ inline int chain_x_chunks(int C) { return C <= 128 ? 128 : (C <= 256 ? 256 : 512); }
 // Bytes of LDS one GEMV's staged x takes: 64 bytes of bf16 pairs and one
 // FP32 sum per (padded) chunk.
 __host__ __device__ inline int chain_x_lds_bytes(int C) { return 68 * chain_x_chunks(C); }

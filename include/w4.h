@@ -187,9 +187,9 @@ W4_API void w4_graph_destroy(w4_graph_t graph);
  * overlap any weight, scale or zero of the chain, any other output, or any
  * input of its own stage (W4_ERR_ALIAS).  The x vectors of one stage must
  * fit the kernel's LDS staging area: the sum over the stage's distinct
- * inputs (GEMVs with the same x share one copy) of
- * 68 * ceil(K / 4096) * 128 bytes at most 65536 (W4_ERR_SHAPE from
- * w4_chain_create otherwise).
+ * inputs (GEMVs with the same x share one copy) of 68 * P bytes, with
+ * P = 128 for K <= 4096, 256 for K <= 8192 and 512 above, at most 65536
+ * (W4_ERR_SHAPE from w4_chain_create otherwise).
  * At most 65534 stages.
  *
  * w4_chain_workspace_bytes(descs, count) validates the descriptors and

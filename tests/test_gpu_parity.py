@@ -462,7 +462,9 @@ def test_chain_two_decoder_layers():
 def test_chain_mixed_shapes():
     """Stages mixing K classes (one, two and four waves per row), ragged N and tiny stages."""
     plan = [[(128, 1), (1024, 7)], [(8192, 100)], [(4096, 1000), (15360, 3), (256, 33)], [(16384, 9)],
-            [(3840, 2)], [(512, 4096), (2048, 77)]]
+            [(3840, 2)], [(512, 4096), (2048, 77)],
+            # rows of 260 and 384 chunks: four segments, the last one all padding
+            [(8320, 6), (640, 5)], [(12288, 3)]]
     gemvs, refs = [], []
     for st, group in enumerate(plan):
         for j, (K, N) in enumerate(group):
