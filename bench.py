@@ -23,9 +23,14 @@ Also reported, outside the timed step:
     its own N(0,1) input (no GEMV waits for another), in one chain launch;
   * ``extra.decode_step_336_launch_graph``: the same step as a graph of 336
     separate w4_gemv launches, with per-shape kernel timings;
-  * ``extra``: the single 3840 x 3840 GEMV, the 262144-row logits GEMV, the
-    two M = 128 prefill GEMMs (TFLOP/s) and the six-expert FP4 MoE pair,
-    each replayed over rotated weight copies so the data comes from HBM;
+  * ``extra``: the single 3840 x 3840 GEMV (and one cold launch of it), the
+    262144-row logits GEMV, the two M = 128 prefill GEMMs (TFLOP/s) and the
+    six-expert FP4 MoE pair, each replayed over rotated weight copies so the
+    data comes from HBM (medians of 5 trials);
+  * ``extra.hbm_read_probe``: the read rate of a plain streaming read kernel
+    over 2 GiB, the measured ceiling for the weight-streaming kernels, and
+    ``extra.empty_336_launch_graph_us``, a graph of 336 empty launches (the
+    launch floor of the 336-launch step);
   * ``cpu_baseline``: the FP64 oracle timed on host cores on a sample of the
     same step.
 
@@ -128,18 +133,41 @@ def linked_copy(lins):
     return out
 
 
-def time_graph(torch, replay, stream, reps: int, warmup: int = 2):
-    """Milliseconds per replay, from HIP events on ``stream`` around ``reps`` replays."""
+def time_graph(torch, replay, stream, reps: int, warmup: int = 2, trials: int = 5):
+    """Milliseconds per replay: the median over ``trials`` of HIP events on ``stream`` around ``reps`` replays."""
     for _ in range(warmup):
         replay()
     stream.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(reps):
-        replay()
-    b.record(stream)
-    b.synchronize()
-    return a.elapsed_time(b) / reps
+    per = []
+    for _ in range(trials):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            replay()
+        b.record(stream)
+        b.synchronize()
+        per.append(a.elapsed_time(b) / reps)
+    return sorted(per)[len(per) // 2]
+
+
+def floors(w4, torch, stream):
+    """Measured ceilings for context: the HBM read rate of a plain streaming read kernel over
+    2 GiB (well past the 256 MB MALL), and a graph of 336 empty launches (the launch floor of
+    the 336-launch decode step)."""
+    src = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    src.fill_(0x5A)
+    sink = torch.zeros(w4.READ_PROBE_SINK, dtype=torch.int32, device="cuda")
+    ms = time_graph(torch, lambda: w4.w4_read_probe(src, sink, stream=stream), stream, reps=5)
+    read_gbps = src.numel() / (ms * 1e-3) / 1e9
+    g = capture(w4, torch, stream, lambda: [w4.w4_read_probe(src, sink, 0, stream=stream) for _ in range(336)])
+    empty_ms = time_graph(torch, lambda: g.replay(stream), stream, reps=20)
+    g.destroy()
+    log(f"read probe: {read_gbps:.0f} GB/s over 2 GiB; 336 empty launches: {empty_ms * 1e3:.1f} us per replay")
+    return src, sink, {"hbm_read_probe": {"GBps": round(read_gbps, 1), "frac_hbm": round(read_gbps / 8000.0, 4),
+                                          "bytes": src.numel(),
+                                          "note": "plain streaming read kernel of this library (w4_read_probe); "
+                                                  "median of 5 trials of 5 launches"},
+                       "empty_336_launch_graph_us": round(empty_ms * 1e3, 1)}
 
 
 def capture(w4, torch, stream, body):
@@ -167,8 +195,8 @@ def per_launch_durations(w4, torch, step):
 
 def extra_workloads(w4, host, si, torch, rf):
     """Other workloads, each as a graph over rotated weight copies (>= 512 MB walked)."""
-    out = {}
     stream = torch.cuda.Stream()
+    flush_src, flush_sink, out = floors(w4, torch, stream)
     MB = 1 << 20
 
     # single 3840 x 3840 GEMV
@@ -186,11 +214,20 @@ def extra_workloads(w4, host, si, torch, rf):
     ms = time_graph(torch, lambda: g.replay(stream), stream, reps=20)
     us = ms * 1e3 / n_copies
     gbps = rf.int4_linear_bytes(K, N) / (us * 1e-6) / 1e9
+    # one cold launch: the GEMV's weights evicted from every cache by a 2 GiB read first
+    w4.w4_read_probe(flush_src, flush_sink, stream=stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    w4.w4_gemv(x, copies[0]["qw"], copies[0]["s"], copies[0]["z"], y, stream=stream)
+    b.record(stream)
+    b.synchronize()
+    cold_us = a.elapsed_time(b) * 1e3
     out["single_gemv_3840x3840"] = {"us_per_call": round(us, 3), "GBps": round(gbps, 1),
-                                    "frac_hbm": round(gbps / rf.HBM_PEAK_GBPS, 4), "copies": n_copies}
+                                    "frac_hbm": round(gbps / rf.HBM_PEAK_GBPS, 4), "copies": n_copies,
+                                    "cold_launch_us": round(cold_us, 2)}
     g.destroy()
     del copies
-    log(f"single GEMV 3840x3840: {us:.2f} us, {gbps:.0f} GB/s")
+    log(f"single GEMV 3840x3840: {us:.2f} us, {gbps:.0f} GB/s; one cold launch {cold_us:.1f} us")
 
     # logits GEMV 3840 -> 262144
     K, N = si.LOGITS_SHAPE

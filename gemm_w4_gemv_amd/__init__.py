@@ -71,12 +71,15 @@ SIGNATURES = {
     "w4_chain_destroy": (None, [_vp]),
     "w4_dequant_int4": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
     "w4_dequant_fp4": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _vp]),
+    "w4_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
 }
+
+READ_PROBE_SINK = 4096
 
 
 def _load() -> ctypes.CDLL:
     if not LIB_PATH.exists():
-        raise ImportError(f"{LIB_PATH} is not built: run `python -m gemm_w4_gemv_amd.build` "
+        raise ImportError(f"{LIB_PATH} is not built: run `python gemm_w4_gemv_amd/build.py` "
                           "(or __graft_entry__.build()) first")
     handle = ctypes.CDLL(str(LIB_PATH))
     for name, (res, args) in SIGNATURES.items():
@@ -344,3 +347,20 @@ def w4_dequant_fp4(qw_fp4, s_fp4, out_f32=None, out_bf16=None, stream=None) -> N
             raise ValueError(f"outputs must be [N, K] = {(N, K)}")
     _check(lib.w4_dequant_fp4(_dev(qw_fp4, "qw_fp4", _U8), _dev(s_fp4, "s_fp4", _BF16), pf, pb, K, N,
                               _stream(stream)), "w4_dequant_fp4")
+
+
+def w4_read_probe(src, sink, nbytes: int | None = None, stream=None) -> None:
+    """Measurement only: stream ``nbytes`` (default: all) of ``src`` once; one digest word per workgroup into ``sink``.
+
+    ``sink`` is a device uint32 tensor of at least READ_PROBE_SINK words.  With
+    nbytes = 0 the call is one empty launch.
+    """
+    if not (isinstance(src, torch.Tensor) and src.is_cuda and src.is_contiguous()):
+        raise ValueError("src must be a contiguous device tensor")
+    if not (isinstance(sink, torch.Tensor) and sink.is_cuda and sink.dtype == torch.int32 and sink.numel() >= READ_PROBE_SINK):
+        raise ValueError(f"sink must be a device int32 tensor of at least {READ_PROBE_SINK} words")
+    total = src.numel() * src.element_size()
+    n = total if nbytes is None else int(nbytes)
+    if n < 0 or n > total:
+        raise ValueError(f"nbytes must lie in [0, {total}]")
+    _check(lib.w4_read_probe(src.data_ptr(), n, sink.data_ptr(), _stream(stream)), "w4_read_probe")

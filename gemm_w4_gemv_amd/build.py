@@ -4,8 +4,11 @@ Each ``.hip`` file is compiled to an object under ``_build/`` in parallel,
 then linked into ``gemm_w4_gemv_amd/libw4.so``, next to this file.  No GPU is
 needed: hipcc cross-compiles for gfx950.
 
-    python -m gemm_w4_gemv_amd.build            # build
-    python -m gemm_w4_gemv_amd.build --asm      # also write device assembly (.s)
+    python gemm_w4_gemv_amd/build.py            # build
+    python gemm_w4_gemv_amd/build.py --asm      # also write device assembly (.s)
+
+(Run it as a script, or through ``__graft_entry__.build()``: importing the
+package first would load the library this builds.)
 """
 from __future__ import annotations
 

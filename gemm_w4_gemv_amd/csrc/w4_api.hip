@@ -418,6 +418,17 @@ W4_API w4_status w4_chain_error(w4_chain_t chain, uint32_t* error_word) {
 
 W4_API void w4_chain_destroy(w4_chain_t chain) { delete chain; }
 
+W4_API w4_status w4_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+    const char* fn = "w4_read_probe";
+    if (!sink || (!src && bytes)) return fail(W4_ERR_NULL, "%s: sink (and src when bytes > 0) must not be NULL", fn);
+    if (bytes % 16 != 0) return fail(W4_ERR_SHAPE, "%s: bytes = %zu is not a multiple of 16", fn, bytes);
+    if ((src && !aligned(src, 16)) || !aligned(sink, 4)) return fail(W4_ERR_ALIGN, "%s: src (16) or sink (4) misaligned", fn);
+    if (overlap(range(sink, (size_t)W4_READ_PROBE_SINK * 4), range(src, bytes)))
+        return fail(W4_ERR_ALIAS, "%s: sink overlaps the source", fn);
+    hipError_t err = w4::launch_read_probe(src, bytes, sink, W4_READ_PROBE_SINK, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4_OK : hip_fail(err, fn);
+}
+
 W4_API w4_status w4_dequant_int4(const int32_t* qw, const void* s, const void* z, float* out_f32,
                                  void* out_bf16, int K, int N, int g, void* stream) {
     const char* fn = "w4_dequant_int4";

@@ -24,6 +24,8 @@ hipError_t launch_dequant_int4(const int32_t* qw, const void* s, const void* z, 
 hipError_t launch_dequant_fp4(const uint8_t* qw, const void* s, float* out_f32, void* out_bf16,
                               int K, int N, hipStream_t stream);
 
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int sink_words, hipStream_t stream);
+
 // Split of the K range of a GEMV row over the four waves of a workgroup.
 // A row has C = K / 32 chunks of 16 bytes.  Each lane owns up to ``cpl``
 // chunks of one K-slice and keeps their x values in registers; ``slices``

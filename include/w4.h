@@ -234,6 +234,20 @@ W4_API w4_status w4_chain_error(w4_chain_t chain, uint32_t* error_word);
 W4_API void w4_chain_destroy(w4_chain_t chain);
 
 /*
+ * Measurement only: read ``bytes`` of device memory at ``src`` once with
+ * streaming 16-byte loads, as fast as the GPU allows, and write one XOR
+ * digest word per workgroup to ``sink`` (device uint32, W4_READ_PROBE_SINK
+ * words, not read by the host).  The achieved rate is the HBM read ceiling
+ * that the weight-streaming kernels are compared with.  With bytes = 0 it
+ * launches one workgroup that does nothing else, the floor of a launch.
+ * src must be 16-byte aligned and bytes a multiple of 16.  Asynchronous on
+ * ``stream``; capturable.  Errors: W4_ERR_NULL, W4_ERR_ALIGN, W4_ERR_SHAPE,
+ * W4_ERR_ALIAS (sink inside the source), W4_ERR_HIP.
+ */
+#define W4_READ_PROBE_SINK 4096
+W4_API w4_status w4_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
+/*
  * Test-only dequantisers, sharing the device unpack code of the GEMM and the
  * FP4 GEMV.  They write the FP32 value of every weight (exact: at most 15
  * significant bits) and/or its BF16 round-to-nearest-even, so the packed

@@ -484,3 +484,18 @@ def test_chain_mixed_shapes():
             check_outputs(host.bf16_values(t["y"]), y_ref, xn, wmax, what)
     assert step.chain.error() == 0
     step.destroy()
+
+
+def test_read_probe_reads_every_word():
+    """The read probe folds every 32-bit word of the range into its workgroup digests exactly once:
+    the XOR of the digests equals the XOR of the words (ragged sizes and one past the sink's width)."""
+    gen = torch.Generator().manual_seed(11)
+    for nbytes in (16, 4096 + 48, 3 * 256 * 16 * 4096 + 32):
+        words = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, generator=gen)
+        src = words.to(DEV)
+        sink = torch.zeros(w4.READ_PROBE_SINK, dtype=torch.int32, device=DEV)
+        w4.w4_read_probe(src, sink)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        want = np.bitwise_xor.reduce(words.numpy().view(np.uint32))
+        assert got == want, f"{nbytes} bytes"
