@@ -12,41 +12,35 @@
 // 张量核心加速" (its last paragraph).
 //
 // The chain is a list of stages.  GEMVs of one stage are independent (q, k, v;
-// gate, up); a GEMV of stage s may read what stages < s wrote.  One
-// 1024-thread workgroup runs per compute unit, its 16 waves in three roles:
+// gate, up); a GEMV of stage s may read, as its x, the output of a GEMV of an
+// earlier stage.  One 1024-thread workgroup runs per compute unit, its 16
+// waves in two roles:
 //
 //  * kChainComputeWaves compute waves.  The tiles of each stage are split
 //    evenly over all compute waves of the GPU.  A tile is kChainTileRows
 //    slot-rows of 2 chunks (16 bytes of codes) per lane; x comes from LDS.
-//    A wave keeps one tile in flight: it computes a tile, stores its rows
-//    with device-coherent (sc1, write-through) stores, and only then issues
-//    the next tile's loads, so at its last tile of a stage vmcnt(loads just
-//    issued) proves its stores complete while the next stage's weights are
-//    already loading across the stage barrier.  A tile two or more stages
-//    ahead waits until the stage before it is released, so weights reach
-//    HBM in stage order.  Memory parallelism comes from the number of waves
-//    (a deeper per-wave ring makes the compiler's wait counts conservative
-//    at the loop head, and a deeper queue delays the barrier's own loads).
-//    Each wave publishes how many stages it has finished in an LDS word.
-//  * One control wave.  Once every compute wave of its workgroup has
-//    finished stage s, it announces that on its own 128-byte flag line.  The
-//    control wave of workgroup 0 also coordinates: it waits for every
-//    workgroup's flag and publishes the stage count on 64 "go" lines, each
-//    polled by a few control waves.  All flag accesses are relaxed
-//    device-scope atomics; no L2 write-back or invalidate is ever issued
-//    (about 2 us per stage barrier on MI355X, against 15-90 us for a counter
-//    or fence based grid barrier).
-//  * Staging waves (the rest).  They stage each stage's x vectors into one
-//    of two LDS buffers, converted once into the dot2 pair layout, splitting
-//    the 64-chunk slots between them so that the x of a stage arrives in one
-//    round trip.  Inputs from outside the chain are staged as soon as the
-//    buffer is free, while earlier stages run; inputs written by an earlier
-//    stage only after the barrier, with device-coherent loads, and the
-//    control wave takes a share of those.
+//    A wave keeps two tiles in flight in two register sets used in turn:
+//    while one is computed the next one loads, and the set just computed is
+//    refilled with the tile after next (a dummy load of an empty buffer range
+//    past the wave's last tile, so every step issues the same loads and the
+//    compiler's wait counts stay exact).  A wave publishes, in its own LDS
+//    word, how many stages it has finished; it never waits for its own stores.
+//  * Staging waves (the rest).  Stage t's x vectors go into LDS buffer t & 1
+//    in the dot2 pair layout once every compute wave of the workgroup is past
+//    stage t - 2; the staging waves split the stage's 64-chunk slots.  An
+//    input from outside the chain is loaded as soon as the buffer is free.
+//    An input that is an earlier GEMV's output is read from that GEMV's
+//    tagged copy (32-bit words bf16 | tag << 16, written by the producer with
+//    device-coherent stores): the staging waves poll it with device-coherent
+//    loads until every word carries the producer stage's tag of this launch,
+//    starting once their own workgroup has finished the producing stage.
 //
-// Every wait is bounded: past the spin limit the waiter records an error in
-// the workspace and leaves (or, for a compute wave, goes on without waiting),
-// so the launch always ends.
+// So a GEMV waits for exactly the outputs it reads, and nothing else
+// synchronises workgroups: there is no grid-wide barrier.  Each workgroup
+// counts its launches in its own workspace line; the count keeps the tags of
+// consecutive launches apart.  Every wait is bounded: past the spin limit
+// the waiter records an error in the workspace and goes on (a staging wave
+// stops staging), so the launch always ends.
 #include "chain.hpp"
 #include "gemv_common.hpp"
 
@@ -252,7 +246,7 @@ __device__ __forceinline__ void compute(const ChainGemv& G, const Work& w, int l
     }
 }
 
-// --------------------------------------------------------------- control wave
+// --------------------------------------------------------------- staging waves
 
 // Slot ``k`` of a stage's x staging: chunks [64 m, 64 m + 64) of GEMV g
 // (slots cover each GEMV's padded chunk count).

@@ -41,9 +41,9 @@ struct ChainStage {
     int x_internal;  // 1: some input of the stage is an output of an earlier GEMV
 };
 
-constexpr int kChainThreads = 1024;  // 16 waves: 1 control, kChainComputeWaves compute, the rest staging
+constexpr int kChainThreads = 1024;  // 16 waves: kChainComputeWaves compute, the rest staging
 constexpr int kChainComputeWaves = 8;
-constexpr int kChainStagers = 16 - kChainComputeWaves;  // staging waves
+constexpr int kChainStagers = kChainThreads / 64 - kChainComputeWaves;  // staging waves
 constexpr int kChainMaxWorkers = 1024;
 constexpr int kChainTileRows = 4;     // slot-rows per compute-wave tile: 4 / sp rows of a GEMV
 constexpr int kChainLineWords = 32;    // one 128-byte line per launch counter
