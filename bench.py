@@ -23,7 +23,8 @@ Also reported, outside the timed step:
     its own N(0,1) input (no GEMV waits for another), in one chain launch;
   * ``extra.decode_step_336_launch_graph``: the same step as a graph of 336
     separate w4_gemv launches, with per-shape kernel timings;
-  * ``extra``: the single 3840 x 3840 GEMV (and one cold launch of it), the
+  * ``extra``: the single 3840 x 3840 GEMV (also one cold launch, and all its
+    rotated copies as one stage of one chain launch), the
     262144-row logits GEMV, the two M = 128 prefill GEMMs (TFLOP/s) and the
     six-expert FP4 MoE pair, each replayed over rotated weight copies so the
     data comes from HBM (medians of 5 trials);
@@ -222,12 +223,27 @@ def extra_workloads(w4, host, si, torch, rf):
     b.record(stream)
     b.synchronize()
     cold_us = a.elapsed_time(b) * 1e3
+    g.destroy()
+    # the same copies as one stage of the persistent chain kernel (one launch, one shared x,
+    # one output each): the shape's streaming rate with the per-launch cost amortised
+    from gemm_w4_gemv_amd.decode import DecodeStep
+    batch = [dict(t, x=x, y=torch.empty(N, dtype=torch.bfloat16, device="cuda"), stage=0) for t in copies]
+    step = DecodeStep(batch, stream=stream, mode="chain")
+    step.capture()
+    ms_b = time_graph(torch, step.replay, stream, reps=20)
+    us_b = ms_b * 1e3 / n_copies
+    gbps_b = rf.int4_linear_bytes(K, N) / (us_b * 1e-6) / 1e9
+    err_b = step.chain.error()
+    step.destroy()
     out["single_gemv_3840x3840"] = {"us_per_call": round(us, 3), "GBps": round(gbps, 1),
                                     "frac_hbm": round(gbps / rf.HBM_PEAK_GBPS, 4), "copies": n_copies,
-                                    "cold_launch_us": round(cold_us, 2)}
-    g.destroy()
-    del copies
-    log(f"single GEMV 3840x3840: {us:.2f} us, {gbps:.0f} GB/s; one cold launch {cold_us:.1f} us")
+                                    "cold_launch_us": round(cold_us, 2),
+                                    "batched_in_one_chain_launch": {
+                                        "us_per_gemv": round(us_b, 3), "GBps": round(gbps_b, 1),
+                                        "frac_hbm": round(gbps_b / rf.HBM_PEAK_GBPS, 4), "error_word": err_b}}
+    del copies, batch
+    log(f"single GEMV 3840x3840: {us:.2f} us, {gbps:.0f} GB/s; one cold launch {cold_us:.1f} us; "
+        f"{n_copies} in one chain launch: {us_b:.2f} us each, {gbps_b:.0f} GB/s")
 
     # logits GEMV 3840 -> 262144
     K, N = si.LOGITS_SHAPE

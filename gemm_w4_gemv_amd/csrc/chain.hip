@@ -104,12 +104,25 @@ __device__ __forceinline__ void set_error(const ChainLaunch& L, Shared& sh, unsi
 
 // Place ``w`` at tile w.t of stage w.s.  Every field is wave-uniform;
 // readfirstlane tells the compiler so, keeping the work state and the buffer
-// descriptors built from it in SGPRs.
-__device__ __forceinline__ void place(const ChainLaunch& L, Work& w) {
+// descriptors built from it in SGPRs.  The GEMV holding the tile is found by
+// a binary search over the stage's tile0 table (ascending) when ``from`` is
+// -1, else by a forward scan from GEMV ``from``, which holds an earlier tile
+// of the same stage (a wave's tiles of a stage are consecutive).
+__device__ __forceinline__ void place(const ChainLaunch& L, Work& w, int from) {
     const ChainStage st = L.stages[w.s];
-    int g = st.gemv0;
-    for (int i = 1; i < st.ngemv; ++i)
-        if (w.t >= L.gemvs[st.gemv0 + i].tile0) g = st.gemv0 + i;
+    int g;
+    if (from < 0) {
+        int lo = st.gemv0, hi = st.gemv0 + st.ngemv - 1;  // the answer lies in [lo, hi]
+        while (lo < hi) {
+            const int mid = uniform((lo + hi + 1) >> 1);
+            if (w.t >= L.gemvs[mid].tile0) lo = mid;
+            else hi = mid - 1;
+        }
+        g = lo;
+    } else {
+        g = from;
+        while (g + 1 < st.gemv0 + st.ngemv && w.t >= L.gemvs[g + 1].tile0) g = uniform(g + 1);
+    }
     g = uniform(g);
     const ChainGemv& G = L.gemvs[g];
     const int rpt = kSlotRows / G.sp;
@@ -130,7 +143,7 @@ __device__ __forceinline__ Work first_from(const ChainLaunch& L, int s, int v, i
             w.s = uniform(s);
             w.t = a;
             w.end = b;
-            place(L, w);
+            place(L, w, -1);
             return w;
         }
     }
@@ -141,7 +154,7 @@ __device__ __forceinline__ Work first_from(const ChainLaunch& L, int s, int v, i
 __device__ __forceinline__ Work advance(const ChainLaunch& L, Work w, int v, int W) {
     w.t = uniform(w.t + 1);
     if (w.t < w.end) {
-        place(L, w);
+        place(L, w, w.g);
         return w;
     }
     return first_from(L, w.s + 1, v, W);
