@@ -18,7 +18,7 @@
 #include "w4_internal.hpp"
 
 #ifndef W4_MOE_MIN_BLOCKS
-#define W4_MOE_MIN_BLOCKS 1024
+#define W4_MOE_MIN_BLOCKS 512  // launch at least this many workgroups when N allows (256-512 measured best for the 6-slot FCs)
 #endif
 
 namespace w4 {
