@@ -73,7 +73,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the FP64 oracle")
-    p.add_argument("--cpu-layers", type=int, default=1, help="decode layers the oracle sample covers")
+    p.add_argument("--cpu-layers", type=int, default=12, help="decode layers the oracle sample covers")
     p.add_argument("--counters", action="store_true",
                    help="run only five chain launches and five 512 MiB copies (for HBM counter runs)")
     return p.parse_args()
@@ -326,10 +326,26 @@ def cpu_baseline(si, rf, layers: int):
         y = oracle.gemv_int4(x, lin["qw"], lin["s"], lin["z"])
         assert np.all(np.isfinite(y))
     dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"decode layers 0..{layers - 1}: {len(inputs)} linears, {nbytes} algorithmic bytes, "
-                      f"{dt:.1f} s (FP64 numpy unpack + dequant + matmul)",
-            "seconds": round(dt, 2)}
+    out = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+           "sample": f"decode layers 0..{layers - 1}: {len(inputs)} linears, {nbytes} algorithmic bytes, "
+                     f"{dt:.1f} s (FP64 numpy unpack + dequant + matmul)",
+           "seconds": round(dt, 2)}
+    # the same oracle on one thread, on layer 0 only
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:
+        return out
+    first = inputs[:len(si.DECODE_LAYER)]
+    nb1 = sum(rf.int4_linear_bytes(lin["qw"].shape[1] * 8, lin["qw"].shape[0]) for lin, _ in first)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for lin, x in first:
+            oracle.gemv_int4(x, lin["qw"], lin["s"], lin["z"])
+        dt1 = time.perf_counter() - t0
+    out["single_thread"] = {"value": round(nb1 / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                            "sample": f"decode layer 0: {len(first)} linears, {nb1} algorithmic bytes",
+                            "seconds": round(dt1, 2)}
+    return out
 
 
 # --------------------------------------------------------------------- main
