@@ -21,10 +21,12 @@
 // is a fixed register set (up to kDepth - 1 surplus steps at the end compute
 // on zeros: loads past the K range use an empty buffer range, which returns
 // zeros without touching memory).  The staging of step j + 1 (dequantise,
-// LDS stores) is spread between step j's MFMAs.  LDS traffic (fragment reads
-// and staging stores, 176 KB per K-step) is what bounds this kernel on
-// MI355X; MFMA issue and global loads are not (removing either leaves the
-// time unchanged).  All loads are buffer loads (weights non-temporal).  When
+// LDS stores) is spread between step j's MFMAs.  LDS is what bounds this
+// kernel on MI355X: 16 fragment reads per wave and 176 KB per K-step, and a
+// 64-lane ds_read_b128 costs about the same time whatever its addresses, so
+// the count of LDS read instructions per MFMA sets the pace; removing the
+// MFMAs leaves the time unchanged.  All loads are buffer loads (weights
+// non-temporal).  When
 // the N x M tiles cannot fill the GPU, K is split; each split writes FP32
 // partials to the caller's workspace and a second kernel adds them in split
 // order (deterministic, no atomics).

@@ -486,6 +486,51 @@ def test_chain_mixed_shapes():
     step.destroy()
 
 
+def test_chain_many_gemvs_per_stage():
+    """Stages of many GEMVs (a tile's GEMV is found by binary search, then by a forward scan):
+    40 GEMVs sharing three inputs in one stage, tiny and ragged N, then 24 GEMVs that read
+    outputs of the first stage."""
+    rng = np.random.default_rng(5)
+    xs = {K: si.bf16_normal(60, (K,), (K,)) for K in (128, 1024, 3840)}
+    xs_dev = {K: host.bf16_tensor(b) for K, b in xs.items()}
+    gemvs, refs, first = [], [], []
+    for j in range(40):
+        K = (128, 1024, 3840)[j % 3]
+        N = int(rng.choice([1, 3, 5, 64, 128, 333, 1024]))
+        lin_np, _ = si.single_gemv(K, N, seed=300 + j)
+        t = host.int4_tensors(lin_np)
+        t["x"], t["y"], t["stage"] = xs_dev[K], torch.zeros(N, dtype=torch.bfloat16, device=DEV), 0
+        y_ref, wmax = int4_ref(lin_np, xs[K])
+        gemvs.append(t)
+        refs.append((y_ref[0], wmax, xnorm(xs[K]), f"stage 0 gemv {j} K={K} N={N}"))
+        first.append((t, oracle.bf16_bits(y_ref[0])))
+    # second stage: each GEMV reads one first-stage output whose length is a valid K
+    # at most six distinct inputs: their staged copies share one stage's LDS budget
+    sources = [(t, yb) for t, yb in first if t["y"].numel() in (128, 1024)][:6]
+    assert sources
+    for j in range(24):
+        src, y_bits = sources[j % len(sources)]
+        K = src["y"].numel()
+        N = int(rng.choice([2, 64, 257]))
+        lin_np, _ = si.single_gemv(K, N, seed=400 + j)
+        t = host.int4_tensors(lin_np)
+        t["x"], t["y"], t["stage"] = src["y"], torch.zeros(N, dtype=torch.bfloat16, device=DEV), 1
+        y_ref, wmax = int4_ref(lin_np, y_bits)
+        gemvs.append(t)
+        refs.append((y_ref[0], wmax, xnorm(y_bits), f"stage 1 gemv {j} K={K} N={N}"))
+    step = DecodeStep(gemvs, mode="chain")
+    for rep in range(2):
+        for t in gemvs:
+            t["y"].zero_()
+        torch.cuda.synchronize()
+        step.run_eager()
+        step.stream.synchronize()
+        for t, (y_ref, wmax, xn, what) in zip(gemvs, refs):
+            check_outputs(host.bf16_values(t["y"]), y_ref, xn, wmax, f"{what} run {rep}")
+    assert step.chain.error() == 0
+    step.destroy()
+
+
 def test_read_probe_reads_every_word():
     """The read probe folds every 32-bit word of the range into its workgroup digests exactly once:
     the XOR of the digests equals the XOR of the words (ragged sizes and one past the sink's width)."""
