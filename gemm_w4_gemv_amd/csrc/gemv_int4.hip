@@ -26,9 +26,14 @@
 #include "gemv_common.hpp"
 #include "w4_internal.hpp"
 
-#ifndef W4_GEMV_MIN_BLOCKS
-#define W4_GEMV_MIN_BLOCKS 1024  // launch at least this many workgroups when N allows
-#endif
+// Rows per wave are the most (8, 4, 2, 1) that still launch at least this
+// many workgroups: fewer, larger workgroups cost less per launch, more of
+// them keep more loads in flight.  Measured on the decode shapes: 256 suits
+// GEMVs under 16 MB of weights (3840 x 3840: 4.2 us instead of 4.8 at 1024),
+// 512 the larger ones (3840 -> 15360: 8.6 us instead of 8.9).
+constexpr int kMinBlocksSmall = 256;
+constexpr int kMinBlocksLarge = 512;
+constexpr size_t kSmallWeightBytes = (size_t)16 << 20;
 
 namespace w4 {
 namespace {
@@ -151,9 +156,10 @@ hipError_t launch_rpt(const void* x, const int32_t* qw, const void* s, const voi
                       int C, int N, hipStream_t stream) {
     constexpr int T = 4 / S;
     auto blocks = [&](int rpt) { return (N + T * rpt - 1) / (T * rpt); };
-    if (blocks(8) >= W4_GEMV_MIN_BLOCKS) return launch_shape<S, CPL, 8>(x, qw, s, z, y, C, N, stream);
-    if (blocks(4) >= W4_GEMV_MIN_BLOCKS) return launch_shape<S, CPL, 4>(x, qw, s, z, y, C, N, stream);
-    if (blocks(2) >= W4_GEMV_MIN_BLOCKS) return launch_shape<S, CPL, 2>(x, qw, s, z, y, C, N, stream);
+    const int min_blocks = (size_t)N * (size_t)C * 16u < kSmallWeightBytes ? kMinBlocksSmall : kMinBlocksLarge;
+    if (blocks(8) >= min_blocks) return launch_shape<S, CPL, 8>(x, qw, s, z, y, C, N, stream);
+    if (blocks(4) >= min_blocks) return launch_shape<S, CPL, 4>(x, qw, s, z, y, C, N, stream);
+    if (blocks(2) >= min_blocks) return launch_shape<S, CPL, 2>(x, qw, s, z, y, C, N, stream);
     return launch_shape<S, CPL, 1>(x, qw, s, z, y, C, N, stream);
 }
 
