@@ -11,7 +11,9 @@ down's (attention and the gate/up product are outside this path).  Values
 grow about 1000x per layer and overflow BF16 after about a dozen layers;
 no kernel's timing depends on the values.  The graph holds one launch of
 the persistent decode-chain kernel, in which each GEMV waits for exactly
-the output it reads.  Inputs are seeded synthetic data already resident in
+the output it reads; each layer runs in six stages, q | k, v | o | gate |
+up | down (k, v and up, read by no later linear here, stream while o's and
+down's inputs are awaited).  Inputs are seeded synthetic data already resident in
 device memory.  ``value`` is the algorithmic bytes of one step (packed
 weights + scales + zeros + x + y, each once) divided by the measured time
 per step.
@@ -108,7 +110,7 @@ def measured_traffic():
 # ------------------------------------------------------------------ helpers
 def decode_linears(host, si, torch):
     """The 336 linears of the decode step, each reading its own seeded N(0,1) input."""
-    from gemm_w4_gemv_amd.decode import LAYER_STAGE
+    from gemm_w4_gemv_amd.decode import decoder_stages
 
     lins = []
     for layer, idx, name, K, N in si.decode_step_specs():
@@ -117,7 +119,7 @@ def decode_linears(host, si, torch):
         t["x"] = host.bf16_tensor(x_bits)
         t["y"] = torch.zeros(N, dtype=torch.bfloat16, device="cuda")
         t["name"], t["layer"], t["K"], t["N"] = name, layer, K, N
-        t["stage"] = 4 * layer + LAYER_STAGE[name]
+        t["stage"] = decoder_stages([name], [layer])[0]
         lins.append(t)
     torch.cuda.synchronize()
     return lins
@@ -402,6 +404,7 @@ def main() -> int:
     log("generating and uploading the decode step (336 INT4 linears)")
     own = decode_linears(host, si, torch)
     lins = linked_copy(own)
+    n_stages = len({l["stage"] for l in lins})
     step_bytes = sum(rf.int4_linear_bytes(l["K"], l["N"]) for l in lins)
     step_flops = sum(rf.flops(1, l["K"], l["N"]) for l in lins)
     step = DecodeStep(lins, mode="chain")
@@ -444,7 +447,7 @@ def main() -> int:
     achieved = step_bytes / (avg_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / rf.HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
-                "kernel": "chain_kernel (336 INT4 GEMVs in 192 stages, each waiting for the output it reads; "
+                "kernel": f"chain_kernel (336 INT4 GEMVs in {n_stages} stages, each waiting for the output it reads; "
                           "one launch per decode step)",
                 "bytes_per_launch": step_bytes, "avg_launch_us": round(avg_us, 2), "launches_timed": reps}
     log(f"chain kernel: {avg_us:.1f} us/launch, {achieved:.0f} GB/s")
@@ -502,7 +505,7 @@ def main() -> int:
                                "(q,k,v,o,gate,up,down; hidden 3840; group 128; M=1), each reading the output "
                                "it reads in a decoder (o<-q, gate/up<-o, down<-gate, next q/k/v<-down), "
                                "run by the persistent chain kernel",
-                   "linears": n_lins, "stages": 192, "bytes_per_step": step_bytes, "flops_per_step": step_flops,
+                   "linears": n_lins, "stages": n_stages, "bytes_per_step": step_bytes, "flops_per_step": step_flops,
                    "us_per_step": round(ms_per_step * 1e3, 1), "gpu_us_per_step": round(gpu_ms_per_step * 1e3, 1),
                    "frac_hbm": round(value / rf.HBM_PEAK_GBPS, 4)},
         "roofline": roofline,

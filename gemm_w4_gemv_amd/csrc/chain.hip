@@ -398,16 +398,19 @@ __device__ __forceinline__ bool lds_wait(const ChainLaunch& L, Shared& sh, F rea
 // stages still run); an input that is an earlier GEMV's output is polled
 // from that GEMV's tagged copy until every word carries its writer's tag,
 // so a stage waits for exactly the outputs it reads and for nothing else.
+// Polling starts once this workgroup has finished the latest stage the
+// inputs come from (x_after), so it overlaps any stage in between.
 // sh.staged[sid] counts the stages this wave has staged.
 __device__ void staging_wave(const ChainLaunch& L, Shared& sh, unsigned char* xl, int lane, int sid) {
     for (int t = 0; t < L.num_stages; ++t) {
         // Buffer free: every compute wave here is past stage t - 2.  A stage
         // that reads earlier outputs also waits until this workgroup's own
-        // part of stage t - 1 is done: by then the other workgroups' parts
-        // are mostly done too, so the polls that follow are few (polling
-        // from the start of stage t - 1 would load the inputs over and over
-        // while the weights stream).
-        const unsigned need = L.stages[t].x_internal ? (unsigned)t : (unsigned)max(t - 1, 0);
+        // part of the producing stage is done: by then the other workgroups'
+        // parts are mostly done too, so the polls that follow are few
+        // (polling from the start of the producing stage would load the
+        // inputs over and over while the weights stream).
+        const ChainStage& st = L.stages[t];
+        const unsigned need = (unsigned)max(t - 1, st.x_internal ? st.x_after + 1 : 0);
         const bool ok = need == 0 || lds_wait(L, sh, [&] {
                             return __builtin_amdgcn_ballot_w64(
                                        lane < kChainComputeWaves &&

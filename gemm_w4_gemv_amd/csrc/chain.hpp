@@ -39,6 +39,7 @@ struct ChainStage {
     int ngemv;
     int tiles;       // total tiles of the stage's GEMVs
     int x_internal;  // 1: some input of the stage is an output of an earlier GEMV
+    int x_after;     // latest stage whose outputs the stage reads (-1: none)
 };
 
 constexpr int kChainThreads = 1024;  // 16 waves: kChainComputeWaves compute, the rest staging

@@ -322,7 +322,7 @@ W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* wor
     for (int i = 0; i < count; ++i) {
         const w4_gemv_desc& d = descs[i];
         if (i == 0 || d.stage != descs[i - 1].stage) {
-            stages.push_back({i, 0, 0, 0});
+            stages.push_back({i, 0, 0, 0, -1});
             x_bytes = 0;
         }
         w4::ChainStage& st = stages.back();
@@ -371,6 +371,7 @@ W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* wor
             const int j = plan.producer[i];
             for (int u = 0; u < num_stages; ++u)
                 if (j >= stages[u].gemv0 && j < stages[u].gemv0 + stages[u].ngemv) gemvs[i].xm_stage = u;
+            if (gemvs[i].xm_stage > stages[t].x_after) stages[t].x_after = gemvs[i].xm_stage;
         }
     int occ = 0, cus = 0, dev = 0;
     hipError_t err = w4::chain_occupancy(&occ);

@@ -24,8 +24,17 @@ import torch
 from . import w4_gemv, w4_graph_begin, w4_graph_end, W4Graph, w4_chain_create, w4_chain_run, \
     w4_chain_workspace_bytes
 
-# stage of each decoder linear within its layer: {q, k, v} -> {o} -> {gate, up} -> {down}
-LAYER_STAGE = {"q": 0, "k": 0, "v": 0, "o": 1, "gate": 2, "up": 2, "down": 3}
+# Stage of each decoder linear within its layer.  Along the decoder's data
+# flow q -> o -> gate -> down -> (next layer's) q each of these waits for the
+# one before; k, v and up are read by no linear of this path, so each pair
+# gets a stage of its own right after the linear that shares its input
+# (k, v after q; up after gate): their weights stream while the chain
+# kernel awaits the next reader's input (o's, down's), instead of delaying it.
+LAYER_STAGES = 6
+LAYER_STAGE = {"q": 0, "k": 1, "v": 1, "o": 2, "gate": 3, "up": 4, "down": 5}
+# The grouped schedule: linears that share an input in one stage.
+LAYER_STAGES_GROUPED = 4
+LAYER_STAGE_GROUPED = {"q": 0, "k": 0, "v": 0, "o": 1, "gate": 2, "up": 2, "down": 3}
 
 
 # the output each decoder linear reads: "h" is the layer's input (the first
@@ -33,9 +42,10 @@ LAYER_STAGE = {"q": 0, "k": 0, "v": 0, "o": 1, "gate": 2, "up": 2, "down": 3}
 DECODER_INPUT = {"q": "h", "k": "h", "v": "h", "o": "q", "gate": "o", "up": "o", "down": "gate"}
 
 
-def decoder_stages(names, layers_of):
+def decoder_stages(names, layers_of, grouped: bool = False):
     """Stage number of every linear, from its name and layer index."""
-    return [4 * layer + LAYER_STAGE[name] for name, layer in zip(names, layers_of)]
+    per, table = (LAYER_STAGES_GROUPED, LAYER_STAGE_GROUPED) if grouped else (LAYER_STAGES, LAYER_STAGE)
+    return [per * layer + table[name] for name, layer in zip(names, layers_of)]
 
 
 def link_decoder_inputs(linears) -> None:

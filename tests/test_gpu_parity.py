@@ -324,14 +324,14 @@ def test_moe_small_shapes_and_determinism():
 
 # ------------------------------------------------------ persistent decode chain
 def _decode_linears(with_stage=True):
-    from gemm_w4_gemv_amd.decode import LAYER_STAGE
+    from gemm_w4_gemv_amd.decode import decoder_stages
     lins, host_in, specs = [], [], si.decode_step_specs()
     for layer, idx, name, K, N in specs:
         lin_np, x_bits = si.decode_linear(layer, idx)
         t = host.int4_tensors(lin_np)
         t["x"] = host.bf16_tensor(x_bits)
         t["y"] = torch.zeros(N, dtype=torch.bfloat16, device=DEV)
-        t["stage"] = 4 * layer + LAYER_STAGE[name]
+        t["stage"] = decoder_stages([name], [layer])[0]
         lins.append(t)
         host_in.append((lin_np, x_bits))
     return specs, lins, host_in
@@ -406,8 +406,10 @@ def test_chain_data_dependent():
     step.destroy()
 
 
-def test_chain_two_decoder_layers():
-    """Two full decoder layers wired as a decoder reads them, as the timed decode step is.
+@pytest.mark.parametrize("grouped", [False, True], ids=["six_stages_per_layer", "grouped_four_stages"])
+def test_chain_two_decoder_layers(grouped):
+    """Two full decoder layers wired as a decoder reads them, as the timed decode step is
+    (both stage schedules: k, v and up in stages of their own, or grouped with q and gate).
 
     q, k and v of layer 0 read one input; o reads q's output, gate and up
     read o's, down reads gate's, layer 1's q, k and v read layer 0's down
@@ -417,7 +419,7 @@ def test_chain_two_decoder_layers():
     The outputs are zeroed before every replay, and the tagged copies keep
     the previous replay's values, so a reader that took a stale copy fails.
     """
-    from gemm_w4_gemv_amd.decode import LAYER_STAGE, link_decoder_inputs
+    from gemm_w4_gemv_amd.decode import decoder_stages, link_decoder_inputs
     shapes = {n: (K, N) for n, K, N in si.DECODE_LAYER}
     x0_bits = si.bf16_normal(9, (0,), (3840,))
     h0 = host.bf16_tensor(x0_bits)
@@ -428,7 +430,7 @@ def test_chain_two_decoder_layers():
             t = host.int4_tensors(lin_np)
             t["x"] = h0
             t["y"] = torch.zeros(N, dtype=torch.bfloat16, device=DEV)
-            t["name"], t["layer"], t["stage"] = name, layer, 4 * layer + LAYER_STAGE[name]
+            t["name"], t["layer"], t["stage"] = name, layer, decoder_stages([name], [layer], grouped)[0]
             gemvs.append(t)
             lin_nps.append(lin_np)
     link_decoder_inputs(gemvs)
