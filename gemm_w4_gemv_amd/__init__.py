@@ -69,6 +69,7 @@ SIGNATURES = {
     "w4_chain_run": (_i32, [_vp, _vp]),
     "w4_chain_error": (_i32, [_vp, ctypes.POINTER(ctypes.c_uint32)]),
     "w4_chain_destroy": (None, [_vp]),
+    "w4_chain_set_spin_limit": (_i32, [_vp, ctypes.c_uint32]),
     "w4_dequant_int4": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
     "w4_dequant_fp4": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _vp]),
     "w4_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
@@ -283,6 +284,10 @@ class W4Chain:
 
     def error(self) -> int:
         return w4_chain_error(self)
+
+    def set_spin_limit(self, spin_limit: int) -> None:
+        """For tests of failure handling: bound every wait of later runs to ``spin_limit`` polls."""
+        _check(lib.w4_chain_set_spin_limit(self.handle, int(spin_limit)), "w4_chain_set_spin_limit")
 
     def destroy(self) -> None:
         if self.handle:

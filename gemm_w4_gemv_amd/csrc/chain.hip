@@ -76,7 +76,8 @@ struct Shared {
     // Stages each staging wave has staged; per wave for the same reason.
     unsigned staged[kChainStagers];
     unsigned abort;
-    unsigned base;      // launches this workgroup has run before this one
+    unsigned timed_out;  // a compute wave stopped waiting for its x (recorded at the end)
+    unsigned base;       // launches this workgroup has run before this one
     unsigned tag_base;  // (base * num_stages) mod 65535
 };
 
@@ -434,7 +435,8 @@ __device__ void compute_wave(const ChainLaunch& L, Shared& sh, const unsigned ch
     };
     // Wait until stage s's x is staged.  On abort or time-out the wave goes on
     // without waiting (the outputs are then undefined; the error word says
-    // so): leaving the tile loop early instead makes the compiler's wait-count
+    // so, bit 8 from a staging wave, bit 16 from a compute wave): leaving the
+    // tile loop early instead makes the compiler's wait-count
     // analysis assume that the prefetched tiles were issued last, and wait for
     // all of them before every tile's math.
     auto staged = [&](int s) {
@@ -450,6 +452,10 @@ __device__ void compute_wave(const ChainLaunch& L, Shared& sh, const unsigned ch
             r = staged(s);
             ab = lds_load(&sh.abort) != 0u;
         }
+        // A time-out is noted in LDS (an abort was recorded by whoever set
+        // it); the workgroup writes the error bit at its end, so no global
+        // store joins the tile loop.
+        if (!r & !ab) __hip_atomic_store(&sh.timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     };
 
     Work a = first_from(L, 0, v, W);
@@ -516,6 +522,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainStage* 
         for (int i = 0; i < kChainComputeWaves; ++i) sh.progress[i] = 0;
         for (int i = 0; i < kChainStagers; ++i) sh.staged[i] = 0;
         sh.abort = 0;
+        sh.timed_out = 0;
         sh.base = L.counters[(size_t)blockIdx.x * kChainLineWords];
         sh.tag_base = (sh.base % 65535u) * ((unsigned)L.num_stages % 65535u) % 65535u;
     }
@@ -529,7 +536,10 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainStage* 
     // Every wave has left its loop (all waits are bounded): count the launch.
     // The next launch of the chain reads the counter only after this one ends.
     __syncthreads();
-    if (tid == 0) L.counters[(size_t)blockIdx.x * kChainLineWords] = sh.base + 1u;
+    if (tid == 0) {
+        L.counters[(size_t)blockIdx.x * kChainLineWords] = sh.base + 1u;
+        if (sh.timed_out) __hip_atomic_fetch_or(L.err, 16u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 }  // namespace

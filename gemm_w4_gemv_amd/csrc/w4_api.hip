@@ -410,6 +410,12 @@ W4_API w4_status w4_chain_run(w4_chain_t chain, void* stream) {
     return err == hipSuccess ? W4_OK : hip_fail(err, "w4_chain_run");
 }
 
+W4_API w4_status w4_chain_set_spin_limit(w4_chain_t chain, uint32_t spin_limit) {
+    if (!chain) return fail(W4_ERR_ARG, "w4_chain_set_spin_limit: chain must not be NULL");
+    chain->launch.spin_limit = spin_limit;
+    return W4_OK;
+}
+
 W4_API w4_status w4_chain_error(w4_chain_t chain, uint32_t* error_word) {
     if (!chain || !error_word) return fail(W4_ERR_ARG, "w4_chain_error: chain and error_word must not be NULL");
     hipError_t err = hipDeviceSynchronize();

@@ -232,6 +232,14 @@ W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* wor
 W4_API w4_status w4_chain_run(w4_chain_t chain, void* stream);
 W4_API w4_status w4_chain_error(w4_chain_t chain, uint32_t* error_word);
 W4_API void w4_chain_destroy(w4_chain_t chain);
+/*
+ * For tests of failure handling: bound every wait of the chain's later runs
+ * to ``spin_limit`` polls (default 1 << 20, about a second).  With 0 a run
+ * gives up at the first wait that is not already satisfied: it records a
+ * non-zero error word, leaves the outputs undefined and still ends normally.
+ * Errors: W4_ERR_ARG (chain is NULL).
+ */
+W4_API w4_status w4_chain_set_spin_limit(w4_chain_t chain, uint32_t spin_limit);
 
 /*
  * Measurement only: read ``bytes`` of device memory at ``src`` once with

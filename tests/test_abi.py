@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for name in names:
         assert hasattr(lib, name), f"libw4.so does not export {name}"
         assert name in w4.SIGNATURES, f"binding has no signature for {name}"
@@ -128,6 +128,10 @@ def test_graph_and_dequant_validation():
     assert lib.w4_dequant_int4(QW, S, Z, Y, None, 200, 4, 128, None) == SHAPE
     assert lib.w4_dequant_fp4(QW, S, None, None, 64, 4, None) == NULL
     assert lib.w4_dequant_fp4(QW, S, Y, None, 48, 4, None) == SHAPE
+
+
+def test_chain_spin_limit_validation():
+    assert lib.w4_chain_set_spin_limit(None, 0) == ARG
 
 
 def test_read_probe_validation():

@@ -533,6 +533,41 @@ def test_chain_many_gemvs_per_stage():
     step.destroy()
 
 
+def test_chain_wait_limit_reports_error_and_recovers():
+    """Failure handling, forced from the host: with a spin limit of 0 the first wait that is not
+    already satisfied gives up, so the run records a non-zero error word and still ends (every
+    wave leaves its loop); a chain planned again on the same workspace then runs correctly.
+    Stage 0 has more tiles than the GPU has compute waves, so every workgroup's stage-1 staging
+    must wait for it."""
+    lin0, x_bits = si.single_gemv(3840, 15360, seed=71)
+    lin1 = si.int4_linear(72, (1,), 15360, 512)
+    t0, t1 = host.int4_tensors(lin0), host.int4_tensors(lin1)
+    t0["x"], t0["y"], t0["stage"] = host.bf16_tensor(x_bits), torch.zeros(15360, dtype=torch.bfloat16, device=DEV), 0
+    t1["x"], t1["y"], t1["stage"] = t0["y"], torch.zeros(512, dtype=torch.bfloat16, device=DEV), 1
+    gemvs = [t0, t1]
+    nbytes = w4.w4_chain_workspace_bytes(gemvs)
+    ws = torch.zeros(nbytes + 256, dtype=torch.uint8, device=DEV)
+    off = (-ws.data_ptr()) % 256
+    chain = w4.w4_chain_create(gemvs, ws[off:off + nbytes])
+    chain.set_spin_limit(0)
+    chain.run()
+    torch.cuda.synchronize()
+    assert chain.error() != 0
+    chain.destroy()
+    chain = w4.w4_chain_create(gemvs, ws[off:off + nbytes])
+    for t in gemvs:
+        t["y"].zero_()
+    chain.run()
+    torch.cuda.synchronize()
+    assert chain.error() == 0
+    y0_ref, w0max = int4_ref(lin0, x_bits)
+    check_outputs(host.bf16_values(t0["y"]), y0_ref[0], xnorm(x_bits), w0max, "stage 0 after recovery")
+    y0_bits = oracle.bf16_bits(y0_ref[0])
+    y1_ref, w1max = int4_ref(lin1, y0_bits)
+    check_outputs(host.bf16_values(t1["y"]), y1_ref[0], xnorm(y0_bits), w1max, "stage 1 after recovery")
+    chain.destroy()
+
+
 def test_read_probe_reads_every_word():
     """The read probe folds every 32-bit word of the range into its workgroup digests exactly once:
     the XOR of the digests equals the XOR of the words (ragged sizes and one past the sink's width)."""
