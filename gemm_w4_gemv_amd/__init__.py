@@ -25,7 +25,7 @@ __all__ = [
     "w4_graph_begin", "w4_graph_end", "w4_graph_replay", "w4_graph_destroy", "W4Graph",
     "w4_dequant_int4", "w4_dequant_fp4", "INT4_GROUP", "FP4_GROUP", "GEMV_MAX_K",
     "GemvDesc", "W4Chain", "w4_chain_workspace_bytes", "w4_chain_create", "w4_chain_run",
-    "w4_chain_error", "w4_chain_destroy", "CHAIN_MAX_K",
+    "w4_chain_error", "w4_chain_destroy", "CHAIN_MAX_K", "w4_read_probe", "READ_PROBE_SINK",
 ]
 
 LIB_PATH = pathlib.Path(__file__).resolve().with_name("libw4.so")
