@@ -40,6 +40,9 @@ def flags(extra=()) -> list[str]:
         f"-I{ROOT / 'include'}", f"-I{CSRC}",
         # no packed-FP32 instructions anywhere in the device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in ordinary VGPRs: the prefill GEMM's 128 accumulator
+        # registers otherwise bounce between AGPRs and VGPRs inside its K loop
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-Wall", "-Wno-unused-command-line-argument",
         *extra,
     ]

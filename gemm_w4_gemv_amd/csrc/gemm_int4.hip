@@ -4,221 +4,268 @@
 // "Lab 5: Gemma4 端到端推理优化", section "Triton 反量化 + cuBLAS": the prefill
 // path dequantised the INT4 weight to BF16 and handed it to a tensor-core
 // GEMM, writing and re-reading the whole BF16 weight in device memory.  Here
-// the dequantised tile only ever exists in LDS: each K-step of 128 (one
-// quantisation group) unpacks a 64 x 128 weight tile, computes
-// bf16((q - z) * s) with round-to-nearest-even, stores it in LDS, and the
-// eight waves of the workgroup feed it to v_mfma_f32_16x16x32_bf16 as the B
-// operand.  The activation tile (A operand, 128 x 128 per K-step) is loaded
-// once per workgroup with full-line loads and staged in LDS beside it.
+// the weight is dequantised in registers, straight into the B operand of
+// v_mfma_f32_16x16x32_bf16, and never exists as BF16 outside them.
 //
-// Tile: 128 (M) x 64 (N) per workgroup; wave w computes rows 32 (w % 4) ..
-// +32 and columns 32 (w / 4) .. +32 as 2 x 2 MFMA blocks of 16 x 16.  The
-// activation and dequantised weight tiles are double-buffered in LDS, with
-// one barrier per K-step of 128.  Global loads run kDepth K-steps ahead of
-// the MFMAs: this thread's 64 bytes of the next kDepth activation tiles and
-// its packed weights, scales and zeros of the next kDepth weight tiles live
-// in a ring of registers, the loop unrolled kDepth times so every ring slot
-// is a fixed register set (up to kDepth - 1 surplus steps at the end compute
-// on zeros: loads past the K range use an empty buffer range, which returns
-// zeros without touching memory).  The staging of step j + 1 (dequantise,
-// LDS stores) is spread between step j's MFMAs.  LDS is what bounds this
-// kernel on MI355X: 16 fragment reads per wave and 176 KB per K-step, and a
-// 64-lane ds_read_b128 costs about the same time whatever its addresses, so
-// the count of LDS read instructions per MFMA sets the pace; removing the
-// MFMAs leaves the time unchanged.  All loads are buffer loads (weights
-// non-temporal).  When
-// the N x M tiles cannot fill the GPU, K is split; each split writes FP32
-// partials to the caller's workspace and a second kernel adds them in split
-// order (deterministic, no atomics).
+// Operand layout of v_mfma_f32_16x16x32_bf16 (lane l, i = l % 16, b = l / 16):
+// A holds row i, k = 8b .. 8b+7 of a 16 x 32 block; B holds column i, the same
+// k.  Eight consecutive k of one weight row are exactly one packed INT4 word
+// (bits 4j .. 4j+3 hold k = 8p + j), so lane (i, b) takes one word of row i
+// and dequantises it in place: bf16((q - z) * s), the product exact in FP32
+// and rounded to nearest even once.
+//
+// Tile: a workgroup of eight waves (two per SIMD) owns 128 (M) x 64 (N)
+// outputs and walks its K range one quantisation group (128 k) per step.
+// Each step's activation tile (128 x 128 bf16, 32 KB) and packed weight tile
+// (64 rows x 64 bytes) are loaded with whole-line loads (each activation load
+// instruction covers 4 rows x 256 bytes) into registers two steps ahead, then
+// stored in LDS (double-buffered, one barrier per step).  Wave w takes the
+// k-slice 32 (w % 4) .. +31 of every group and the 32 output columns
+// 32 (w / 4) .. +31: per step it reads 8 A fragments (16 bytes per lane
+// each) and 2 packed words, and computes 128 x 32 outputs over its slices
+// (8 x 2 MFMA blocks, 64 accumulator registers).  Scales and zeros of the
+// workgroup's 64 rows are staged in LDS once, at the start.  At the end the
+// four k-slice waves' partial sums of each column half are added in a fixed
+// order through LDS.  LDS bandwidth is what bounds it: per step 36 KB of
+// tile stores and 64 KB of A-fragment reads (each A byte is read by the two
+// waves of its k-slice), against 512 cycles of MFMA work per SIMD.
+//
+// When the tiles cannot fill the GPU, K is split across workgroups; each
+// split writes FP32 partials to the caller's workspace and a second kernel
+// adds them in split order (deterministic, no atomics).
+#include "w4.h"
 #include "w4_device.hpp"
 #include "w4_internal.hpp"
 
 namespace w4 {
 namespace {
 
-constexpr int kBM = 128, kBN = 64, kBK = 128;
-constexpr int kThreads = 512;
-constexpr int kDepth = 2;            // K-steps of loads in flight ahead of the MFMAs
-constexpr int kTargetBlocks = 256;   // one workgroup per compute unit of an MI355X
+constexpr int kBM = 128, kBN = 64, kGroup = 128;
+constexpr int kWaves = 8, kThreads = kWaves * kWave;
+constexpr int kRB = kBM / 16, kCB = kBN / 16;     // MFMA row and column blocks per tile
+constexpr int kNH = kWaves / 4, kCBW = kCB / kNH;  // column parts, column blocks per wave
+constexpr int kDepth = 2;                          // steps of global loads in flight in registers
+constexpr int kTargetBlocks = 256;                 // one workgroup per compute unit of an MI355X
+constexpr int kMaxGroups = W4_GEMM_MAX_K / kGroup;
 
-// LDS tiles are rows of kBK bf16 (16 chunks of 16 bytes), chunk c of row r
-// stored at chunk position c ^ (r % 16): the 16 rows an MFMA fragment read
-// touches at one chunk, and the 16 chunks of one row a staging write
-// touches, each land on 16 distinct positions, i.e. on all 64 banks once.
-__device__ __forceinline__ int lds_elem(int row, int chunk) { return row * kBK + ((chunk ^ (row & 15)) << 3); }
+// LDS map (bytes).  During the K loop: two activation tiles, two weight
+// tiles, the raw fp16 scales and zeros of the workgroup's rows.  After it:
+// the eight waves' partial sums, over the tiles.
+constexpr int kXTile = kBM * kGroup * 2;            // 32 KB
+constexpr int kWTile = kBN * kGroup / 2;            // 4 KB
+constexpr int kOffW = 2 * kXTile;
+constexpr int kOffSZ = kOffW + 2 * kWTile;
+constexpr int kSZBytes = 2 * kBN * kMaxGroups * 2;  // s then z, [64][G] fp16 each
+constexpr int kRedBytes = kWaves * kRB * kCBW * kWave * 16;
+constexpr int kLdsBytes = (kOffSZ + kSZBytes) > kRedBytes ? (kOffSZ + kSZBytes) : kRedBytes;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 
 __device__ __forceinline__ void mfma_16x16x32(const u32x4_t& a, const u32x4_t& b, f32x4_t& acc) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
 }
 
-// One ring slot: this thread's share of one K-step's activation tile (chunk
-// tid % 16 of rows tid / 16 + 32 i) and of its packed weight tile (16 codes
-// of one row, with that row's scale and zero).
+// Activation tile: row r, 16-byte chunk c (k = 8c .. 8c+7) at chunk position
+// c ^ (r % 16), so the 16 rows of a fragment read and the 16 chunks of a row
+// store each cover all banks once.
+__device__ __forceinline__ int x_lds(int r, int c) { return (r * 16 + (c ^ (r & 15))) * 16; }
+// Weight tile: row n, word p (0..15) at word 4 ((p / 4) ^ ((n / 4) % 4)) + p % 4.
+__device__ __forceinline__ int w_lds(int n, int p) { return (n * 16 + 4 * ((p >> 2) ^ ((n >> 2) & 3)) + (p & 3)) * 4; }
+
+// One register slot: this thread's share of one step's tiles.
+constexpr int kXL = kRB * 4 / kWaves;  // activation loads per thread per step
 struct Slot {
-    u32x4_t a[4];
-    u32x4_t w;  // .x, .y: codes; .z, .w: scale and zero bits
+    u32x4_t a[kXL];  // activation chunk (tid % 16) of rows tid / 16 + (kThreads / 16) i
+    u32x2_t w;       // weight half-chunk (tid % 8) of row tid / 8
 };
+
+// bf16((q_e - z) * s) for the eight codes of one word, k order kept.
+// fma(q, s, -z s) is exact: q s and z s have at most 15 significant bits and
+// their difference (q - z) s is representable, so the one rounding is the
+// bf16 conversion (round to nearest even).
+__device__ __forceinline__ u32x4_t dequant_word_bf16(uint32_t w, float s, float nzs) {
+    uint32_t lo = w & 0x0F0F0F0Fu;         // codes of k = 8p + 0, 2, 4, 6
+    uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes of k = 8p + 1, 3, 5, 7
+    // Opaque to the optimiser, so each byte converts with one v_cvt_f32_ubyte{0..3}
+    // instead of a bit-field extract and a conversion.
+    asm volatile("" : "+v"(lo), "+v"(hi));
+    u32x4_t r;
+    r.x = pack_bf16x2(fmaf((float)(lo & 0xFFu), s, nzs), fmaf((float)(hi & 0xFFu), s, nzs));
+    r.y = pack_bf16x2(fmaf((float)((lo >> 8) & 0xFFu), s, nzs), fmaf((float)((hi >> 8) & 0xFFu), s, nzs));
+    r.z = pack_bf16x2(fmaf((float)((lo >> 16) & 0xFFu), s, nzs), fmaf((float)((hi >> 16) & 0xFFu), s, nzs));
+    r.w = pack_bf16x2(fmaf((float)(lo >> 24), s, nzs), fmaf((float)(hi >> 24), s, nzs));
+    return r;
+}
 
 template <bool kSplit>
 __global__ __launch_bounds__(kThreads) void gemm_int4_mfma_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ s,
     const uint16_t* __restrict__ z, uint16_t* __restrict__ y, float* __restrict__ ws, int M, int K,
     int N, int splits) {
-    __shared__ __attribute__((aligned(16))) uint16_t wt[2][kBN * kBK];
-    __shared__ __attribute__((aligned(16))) uint16_t at[2][kBM * kBK];
+    __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const int wm = wave & 3, wn = wave >> 2;
+    const int li = lane & 15, lb = lane >> 4;
+    const int wsl = wave & 3, nh = wave >> 2;  // k-slice and N part of this wave
     const int n0 = blockIdx.x * kBN;
     const int m0 = blockIdx.y * kBM;
-    const int KT = K / kBK;
-    const int G = K / kBK;
-    const int kt0 = (int)(((long)blockIdx.z * KT) / splits);
-    const int kt1 = (int)(((long)(blockIdx.z + 1) * KT) / splits);
-    const int nsteps = kt1 - kt0;
-    const int words_per_row = K / 8;
+    const int G = K / kGroup;
+    const int g0 = (int)(((long)blockIdx.z * G) / splits);
+    const int g1 = (int)(((long)(blockIdx.z + 1) * G) / splits);
+    const int nsteps = g1 - g0;
+    const uint32_t row_bytes = (uint32_t)K / 2;
 
-    // Weight-tile loader: thread -> (row r, 16 codes at k = 16 part).  Rows
-    // past N read row N - 1 (never stored).
-    const int lr = tid >> 3, part = tid & 7;
-    const int wr = min(n0 + lr, N - 1);
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qw, (uint32_t)((size_t)N * words_per_row * 4));
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, (uint32_t)((size_t)N * G * 2));
-    const __amdgpu_buffer_rsrc_t rz = make_rsrc(z, (uint32_t)((size_t)N * G * 2));
-    const __amdgpu_buffer_rsrc_t rnone = make_rsrc(qw, 0u);
-    const uint32_t qoff = (uint32_t)(((size_t)wr * words_per_row + 2 * part) * 4);
-    const uint32_t szoff = (uint32_t)((size_t)wr * G * 2);
-
-    // Activation tile loader: chunk tid % 16 of rows tid / 16 + 32 i: each
-    // load instruction covers 4 whole rows (8 whole 128-byte lines).  Rows
-    // past M read row M - 1; their results are never stored.
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)((size_t)M * K * 2));
-    const int ar = tid >> 4, ac = tid & 15;
-    uint32_t aoff[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) aoff[i] = (uint32_t)(((size_t)min(m0 + ar + 32 * i, M - 1) * K + 8 * ac) * 2);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qw, (uint32_t)((size_t)N * row_bytes));
+    const __amdgpu_buffer_rsrc_t rnone = make_rsrc(qw, 0u);
 
-    // Loads of K-step kt0 + j into a slot (an empty range past the split's end).
+    // Scales and zeros of rows n0 .. n0+63 (all G groups; rows past N read 0
+    // and are never stored): contiguous [64 G] fp16 blocks, staged raw.
+    {
+        const uint32_t sz_bytes = (uint32_t)((size_t)N * G * 2);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, sz_bytes);
+        const __amdgpu_buffer_rsrc_t rz = make_rsrc(z, sz_bytes);
+        // 16-byte aligned: n0 is a multiple of 64.  The whole offset is the
+        // lane offset, which the buffer range check covers.
+        const uint32_t base = (uint32_t)n0 * (uint32_t)G * 2u;
+        const int chunks = kBN * G * 2 / 16;  // per array
+        for (int c = tid; c < chunks; c += kThreads) {
+            const uint32_t off = base + (uint32_t)c * 16u;
+            u32x4_t vs, vz;
+            if (off + 16u <= sz_bytes) {
+                vs = buf_load_b128(rs, off, 0u);
+                vz = buf_load_b128(rz, off, 0u);
+            } else {
+                // The chunk that straddles the end of the arrays: a 16-byte load
+                // partly out of range reads all zeros, so take it 2 bytes at a
+                // time (halves at or past the end read 0).
+                uint32_t hs[8], hz[8];
+#pragma unroll
+                for (int h = 0; h < 8; ++h) {
+                    hs[h] = buf_load_u16(rs, off + 2u * h, 0u);
+                    hz[h] = buf_load_u16(rz, off + 2u * h, 0u);
+                }
+                vs = u32x4_t{hs[0] | hs[1] << 16, hs[2] | hs[3] << 16, hs[4] | hs[5] << 16, hs[6] | hs[7] << 16};
+                vz = u32x4_t{hz[0] | hz[1] << 16, hz[2] | hz[3] << 16, hz[4] | hz[5] << 16, hz[6] | hz[7] << 16};
+            }
+            *reinterpret_cast<u32x4_t*>(lds + kOffSZ + c * 16) = vs;
+            *reinterpret_cast<u32x4_t*>(lds + kOffSZ + kBN * G * 2 + c * 16) = vz;
+        }
+    }
+    const uint16_t* lds_s = reinterpret_cast<const uint16_t*>(lds + kOffSZ);
+    const uint16_t* lds_z = lds_s + kBN * G;
+
+    // Global loaders.  Activations: chunk tid % 16 of rows tid / 16 + 16 i
+    // (rows past M read row M - 1, never stored).  Weights: chunk tid % 4 of
+    // row tid / 4 (rows past N read row N - 1).
+    const int xr = tid >> 4, xc = tid & 15;
+    constexpr int kXRows = kThreads / 16;
+    uint32_t xoff[kXL];
+#pragma unroll
+    for (int i = 0; i < kXL; ++i) xoff[i] = (uint32_t)(((size_t)min(m0 + xr + kXRows * i, M - 1) * K + 8 * xc) * 2);
+    const int wr = tid >> 3, wc = tid & 7;
+    const uint32_t woff = (uint32_t)min(n0 + wr, N - 1) * row_bytes + 8u * wc;
+
     auto issue = [&](int j, Slot& S) {
         const bool live = j < nsteps;
-        const int kt = kt0 + (live ? j : 0);
+        const uint32_t g = (uint32_t)(g0 + (live ? j : 0));
         const __amdgpu_buffer_rsrc_t ra = live ? rx : rnone;
-        const __amdgpu_buffer_rsrc_t rqq = live ? rq : rnone;
-        const __amdgpu_buffer_rsrc_t rss = live ? rs : rnone;
-        const __amdgpu_buffer_rsrc_t rzz = live ? rz : rnone;
+        const __amdgpu_buffer_rsrc_t rw = live ? rq : rnone;
+        S.w = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rw, (int)woff, (int)sgpr(g * 64u), kAuxNontemporal));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S.a[i] = buf_load_b128(ra, aoff[i], (uint32_t)(kt * kBK) * 2u);
-        const u32x2_t q = __builtin_bit_cast(
-            u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rqq, (int)qoff, (int)sgpr((uint32_t)kt * 64u), kAuxNontemporal));
-        S.w.x = q.x;
-        S.w.y = q.y;
-        S.w.z = buf_load_u16(rss, szoff, (uint32_t)kt * 2u);
-        S.w.w = buf_load_u16(rzz, szoff, (uint32_t)kt * 2u);
+        for (int i = 0; i < kXL; ++i) S.a[i] = buf_load_b128(ra, xoff[i], g * 256u);
     };
-    // Staging of one K-step into LDS buffer ``buf``, in four parts that the
-    // main loop interleaves with its MFMAs: dequantise this thread's 16 codes
-    // (part 0) and store them (1), store its activations (2, 3).
-    u32x4_t wlo, whi;
-    auto stage = [&](const Slot& S, int buf, int part_no) {
-        if (part_no == 0) {
-            const float sc = f16_to_f32((uint16_t)S.w.z), zp = f16_to_f32((uint16_t)S.w.w);
-            float f[16];
-            int4_word_dequant_f32(S.w.x, sc, zp, f);
-            int4_word_dequant_f32(S.w.y, sc, zp, f + 8);
-            wlo.x = pack_bf16x2(f[0], f[1]);
-            wlo.y = pack_bf16x2(f[2], f[3]);
-            wlo.z = pack_bf16x2(f[4], f[5]);
-            wlo.w = pack_bf16x2(f[6], f[7]);
-            whi.x = pack_bf16x2(f[8], f[9]);
-            whi.y = pack_bf16x2(f[10], f[11]);
-            whi.z = pack_bf16x2(f[12], f[13]);
-            whi.w = pack_bf16x2(f[14], f[15]);
-        } else if (part_no == 1) {
-            *reinterpret_cast<u32x4_t*>(&wt[buf][lds_elem(lr, 2 * part)]) = wlo;
-            *reinterpret_cast<u32x4_t*>(&wt[buf][lds_elem(lr, 2 * part + 1)]) = whi;
-        } else {
+    auto store = [&](const Slot& S, int buf) {
+        *reinterpret_cast<u32x2_t*>(lds + kOffW + buf * kWTile + w_lds(wr, 2 * wc)) = S.w;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int i = 2 * (part_no - 2) + h;
-                *reinterpret_cast<u32x4_t*>(&at[buf][lds_elem(ar + 32 * i, ac)]) = S.a[i];
-            }
-        }
-    };
-    auto store_w = [&](const Slot& S, int buf) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) stage(S, buf, p);
+        for (int i = 0; i < kXL; ++i)
+            *reinterpret_cast<u32x4_t*>(lds + buf * kXTile + x_lds(xr + kXRows * i, xc)) = S.a[i];
     };
 
-    f32x4_t acc[2][2];
+    f32x4_t acc[kRB][kCBW];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int r = 0; r < kRB; ++r)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < kCBW; ++c) acc[r][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Step j (0-based within the split) computes from LDS buffer j & 1; before
-    // its barrier it stages step j + 1 (slot (j + 1) % kDepth) into the other
-    // buffer, then refills slot j % kDepth with step j + kDepth.
+    // Step j computes group g0 + j from LDS buffer j & 1.  Before it, the
+    // register slot holding step j + 1 was stored into the other buffer and
+    // refilled with step j + 1 + kDepth.
     Slot ring[kDepth];
-    if (nsteps > 0) {
 #pragma unroll
-        for (int d = 0; d < kDepth; ++d) issue(d, ring[d]);
-        store_w(ring[0], 0);
-        __syncthreads();
-        for (int j0 = 0; j0 < nsteps; j0 += kDepth) {
+    for (int d = 0; d < kDepth; ++d) {
+        issue(d, ring[d]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    store(ring[0], 0);
+    issue(kDepth, ring[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    for (int j0 = 0; j0 < nsteps; j0 += kDepth) {
 #pragma unroll
-            for (int d = 0; d < kDepth; ++d) {
-                const int j = j0 + d;
-                const int buf = j & 1;
-                Slot& S = ring[d];
-                const Slot& T = ring[(d + 1) % kDepth];
-                // All fragments of the step first, so the LDS reads overlap
-                // each other rather than each waiting before its MFMAs.
-                u32x4_t a[4][2], b[4][2];
+        for (int d = 0; d < kDepth; ++d) {
+            const int j = j0 + d;
+            const int buf = j & 1;
+            const char* xt = lds + buf * kXTile;
+            const char* wt = lds + kOffW + buf * kWTile;
+            u32x4_t b[kCBW];
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
-                        a[ks][i] = *reinterpret_cast<const u32x4_t*>(
-                            &at[buf][lds_elem(32 * wm + 16 * i + (lane & 15), 4 * ks + (lane >> 4))]);
-#pragma unroll
-                    for (int jj = 0; jj < 2; ++jj)
-                        b[ks][jj] = *reinterpret_cast<const u32x4_t*>(
-                            &wt[buf][lds_elem(32 * wn + 16 * jj + (lane & 15), 4 * ks + (lane >> 4))]);
-                }
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
-#pragma unroll
-                        for (int jj = 0; jj < 2; ++jj) mfma_16x16x32(a[ks][i], b[ks][jj], acc[i][jj]);
-                    // Part ks of step j + 1's staging runs while these MFMAs execute.
-                    stage(T, buf ^ 1, ks);
-                }
-                issue(j + kDepth, S);
-                __syncthreads();
+            for (int c = 0; c < kCBW; ++c) {
+                const int n = 16 * (kCBW * nh + c) + li;
+                const uint32_t q = *reinterpret_cast<const uint32_t*>(wt + w_lds(n, 4 * wsl + lb));
+                // A surplus step past the range (nsteps not a multiple of
+                // kDepth) has zero tiles; its scale and zero stay finite.
+                const int gi = g0 + min(j, nsteps - 1);
+                const float sc = f16_to_f32(lds_s[n * G + gi]);
+                const float zp = f16_to_f32(lds_z[n * G + gi]);
+                b[c] = dequant_word_bf16(q, sc, -zp * sc);
             }
+#pragma unroll
+            for (int r = 0; r < kRB; ++r) {
+                const u32x4_t a = *reinterpret_cast<const u32x4_t*>(xt + x_lds(16 * r + li, 4 * wsl + lb));
+#pragma unroll
+                for (int c = 0; c < kCBW; ++c) mfma_16x16x32(a, b[c], acc[r][c]);
+            }
+            Slot& T = ring[(d + 1) % kDepth];
+            store(T, buf ^ 1);
+            issue(j + 1 + kDepth, T);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
         }
     }
 
-    // Output fragment: lane -> column (lane & 15), rows 4 (lane >> 4) + 0..3.
+    // Cross-wave sum: every wave stores its partials, then thread t adds the
+    // four copies of 4-float groups t, t + 256, ... in wave order.
+    float* red = reinterpret_cast<float*>(lds);
+    constexpr int kPer = kRB * kCBW * kWave * 4;  // floats per wave
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int r = 0; r < kRB; ++r)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int n = n0 + 32 * wn + 16 * jj + (lane & 15);
-            if (n >= N) continue;
+        for (int c = 0; c < kCBW; ++c)
+            *reinterpret_cast<f32x4_t*>(&red[wave * kPer + ((r * kCBW + c) * kWave + lane) * 4]) = acc[r][c];
+    __syncthreads();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int m = m0 + 32 * wm + 16 * i + 4 * (lane >> 4) + e;
-                if (m >= M) continue;
-                if constexpr (kSplit) {
-                    ws[((size_t)blockIdx.z * M + m) * N + n] = acc[i][jj][e];
-                } else {
-                    y[(size_t)m * N + n] = f32_to_bf16(acc[i][jj][e]);
-                }
+    for (int i = tid; i < kNH * kPer / 4; i += kThreads) {
+        // i = (part * kRB * kCBW + r * kCBW + c) * 64 + l: rows 16 r + 4 (l / 16) + e,
+        // column 16 (kCBW part + c) + l % 16; summed over the 4 k-slice waves of the part.
+        const int part = i / (kPer / 4), ii = i % (kPer / 4);
+        f32x4_t t = *reinterpret_cast<const f32x4_t*>(&red[(4 * part) * kPer + ii * 4]);
+#pragma unroll
+        for (int w = 1; w < 4; ++w) t += *reinterpret_cast<const f32x4_t*>(&red[(4 * part + w) * kPer + ii * 4]);
+        const int l = ii & (kWave - 1), rc = ii / kWave;
+        const int r = rc / kCBW, c = kCBW * part + rc % kCBW;
+        const int n = n0 + 16 * c + (l & 15);
+        if (n >= N) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int m = m0 + 16 * r + 4 * (l >> 4) + e;
+            if (m >= M) continue;
+            if constexpr (kSplit) {
+                ws[((size_t)blockIdx.z * M + m) * N + n] = t[e];
+            } else {
+                y[(size_t)m * N + n] = f32_to_bf16(t[e]);
             }
         }
     }
@@ -237,10 +284,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 int choose_splits(int M, int K, int N) {
     const long tiles = (long)((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-    const int KT = K / kBK;
+    const int G = K / kGroup;
     int splits = (int)((kTargetBlocks + tiles / 2) / tiles);  // round(target / tiles)
     if (splits < 1) splits = 1;
-    if (splits > KT) splits = KT;
+    if (splits > G) splits = G;
     if (splits > 16) splits = 16;
     return splits;
 }
@@ -248,7 +295,7 @@ int choose_splits(int M, int K, int N) {
 }  // namespace
 
 size_t gemm_int4_workspace_bytes(int M, int K, int N) {
-    if (M <= 0 || N <= 0 || K <= 0 || K % kBK != 0) return 0;
+    if (M <= 0 || N <= 0 || K <= 0 || K % kGroup != 0 || K > W4_GEMM_MAX_K) return 0;
     const int splits = choose_splits(M, K, N);
     return splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }

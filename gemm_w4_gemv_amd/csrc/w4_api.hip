@@ -106,9 +106,12 @@ W4_API w4_status w4_gemm(const void* x, const int32_t* qw, const void* s, const 
                          void* stream) {
     const char* fn = "w4_gemm";
     if (!x || !y) return fail(W4_ERR_NULL, "%s: x and y must not be NULL", fn);
-    w4_status st = check_int4(fn, qw, s, z, K, N, g, 0);
+    w4_status st = check_int4(fn, qw, s, z, K, N, g, W4_GEMM_MAX_K);
     if (st != W4_OK) return st;
     if (M < 0) return fail(W4_ERR_SHAPE, "%s: M = %d is negative", fn, M);
+    if ((unsigned long long)M * (unsigned long long)K * 2ull > W4_GEMV_MAX_MATRIX_BYTES ||
+        (unsigned long long)N * (unsigned long long)(K / 2) > W4_GEMV_MAX_MATRIX_BYTES)
+        return fail(W4_ERR_SHAPE, "%s: M * K * 2 or N * K / 2 exceeds %llu bytes", fn, W4_GEMV_MAX_MATRIX_BYTES);
     if (!aligned(x, 16)) return fail(W4_ERR_ALIGN, "%s: x must be 16-byte aligned", fn);
     if (!aligned(y, 2)) return fail(W4_ERR_ALIGN, "%s: y must be 2-byte aligned", fn);
     const size_t need = w4_gemm_workspace_bytes(M, K, N, g);

@@ -80,6 +80,11 @@ typedef enum w4_status {
 /* Largest packed weight matrix (N * K / 2 bytes, per expert for FP4) of one
  * w4_gemv / w4_moe_gemv call: the kernels address it with 32-bit offsets. */
 #define W4_GEMV_MAX_MATRIX_BYTES 4294967295ull
+/* Largest K accepted by w4_gemm (a workgroup stages the scales and zeros of
+ * its 64 weight rows, all K / 128 groups, in LDS).  The activations
+ * (M * K * 2 bytes) and the packed weights (N * K / 2 bytes) of one call must
+ * each stay within W4_GEMV_MAX_MATRIX_BYTES: 32-bit offsets address them. */
+#define W4_GEMM_MAX_K 32768
 #define W4_INT4_GROUP 128
 #define W4_FP4_GROUP 32
 
@@ -107,13 +112,14 @@ W4_API w4_status w4_gemv(const void* x, const int32_t* qw, const void* s, const 
                          void* y, int K, int N, int g, void* stream);
 
 /*
- * w4_gemm -- prefill GEMM, any M >= 0 (built for M = 128), INT4 weights.
+ * w4_gemm -- prefill GEMM, any M >= 0 (built for M = 128), INT4 weights,
+ * 0 < K <= W4_GEMM_MAX_K.
  *   y[m][n] = bf16( sum_k bf16((q[n][k] - z[n][k/g]) * s[n][k/g]) * x[m][k] )
  * "Lab 5: Gemma4 端到端推理优化", sections "Triton 反量化 + cuBLAS" (prefill:
  * dequantised BF16 weights into a tensor-core GEMM) and "INT4 融合 GEMV"
- * (equivalence tested at M = 128).  Here the weight tile is dequantised into
- * LDS (BF16, round-to-nearest-even, the matrix-core operand) and never
- * written to device memory.
+ * (equivalence tested at M = 128).  Here each packed word is dequantised in
+ * registers straight into the matrix-core operand (BF16, round-to-nearest-
+ * even) and the BF16 weight is never written to device memory.
  *   x   device bf16 [M][K], 16-byte aligned   qw, s, z as for w4_gemv
  *   y   device bf16 [M][N], 2-byte aligned
  *   workspace  device memory of at least w4_gemm_workspace_bytes(M, K, N, g)

@@ -85,6 +85,8 @@ def test_gemm_validation():
     assert lib.w4_gemm(*args(ws=WSP + 4)) == ALIGN
     assert lib.w4_gemm(*args(M=-1)) == SHAPE
     assert lib.w4_gemm(*args(K=15360 + 64)) == SHAPE
+    assert lib.w4_gemm(*args(K=32768 + 128)) == SHAPE     # past W4_GEMM_MAX_K
+    assert lib.w4_gemm(*args(M=65537, K=32768)) == SHAPE  # activations past 32-bit offsets
     assert lib.w4_gemm(*args(g=256)) == UNSUP
     assert lib.w4_gemm(*args(ws=Y)) == ALIAS          # workspace overlaps y
     assert lib.w4_gemm(*args(ws=QW)) == ALIAS         # workspace overlaps the weights
