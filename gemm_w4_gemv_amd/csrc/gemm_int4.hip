@@ -14,21 +14,22 @@
 // and dequantises it in place: bf16((q - z) * s), the product exact in FP32
 // and rounded to nearest even once.
 //
-// Tile: a workgroup of eight waves (two per SIMD) owns 128 (M) x 64 (N)
+// Tile: a workgroup of sixteen waves (four per SIMD) owns 128 (M) x 64 (N)
 // outputs and walks its K range one quantisation group (128 k) per step.
 // Each step's activation tile (128 x 128 bf16, 32 KB) and packed weight tile
 // (64 rows x 64 bytes) are loaded with whole-line loads (each activation load
 // instruction covers 4 rows x 256 bytes) into registers two steps ahead, then
 // stored in LDS (double-buffered, one barrier per step).  Wave w takes the
-// k-slice 32 (w % 4) .. +31 of every group and the 32 output columns
-// 32 (w / 4) .. +31: per step it reads 8 A fragments (16 bytes per lane
-// each) and 2 packed words, and computes 128 x 32 outputs over its slices
-// (8 x 2 MFMA blocks, 64 accumulator registers).  Scales and zeros of the
+// k-slice 32 (w % 4) .. +31 of every group and the 16 output columns
+// 16 (w / 4) .. +15: per step it reads 8 A fragments (16 bytes per lane
+// each) and one packed word, and computes 128 x 16 outputs over its slices
+// (8 MFMA blocks, 32 accumulator registers).  Scales and zeros of the
 // workgroup's 64 rows are staged in LDS once, at the start.  At the end the
-// four k-slice waves' partial sums of each column half are added in a fixed
-// order through LDS.  LDS bandwidth is what bounds it: per step 36 KB of
-// tile stores and 64 KB of A-fragment reads (each A byte is read by the two
-// waves of its k-slice), against 512 cycles of MFMA work per SIMD.
+// four k-slice waves' partial sums of each column block are added in a fixed
+// order through LDS.  Measured on MI355X, neither the matrix cores nor LDS
+// are saturated (about 20 % and 35 % busy); the waves mostly wait on the
+// per-step chain of global load, LDS store, barrier and LDS read, which is
+// why four waves per SIMD run faster than one or two with larger tiles.
 //
 // When the tiles cannot fill the GPU, K is split across workgroups; each
 // split writes FP32 partials to the caller's workspace and a second kernel
@@ -41,7 +42,7 @@ namespace w4 {
 namespace {
 
 constexpr int kBM = 128, kBN = 64, kGroup = 128;
-constexpr int kWaves = 8, kThreads = kWaves * kWave;
+constexpr int kWaves = 16, kThreads = kWaves * kWave;
 constexpr int kRB = kBM / 16, kCB = kBN / 16;     // MFMA row and column blocks per tile
 constexpr int kNH = kWaves / 4, kCBW = kCB / kNH;  // column parts, column blocks per wave
 constexpr int kDepth = 2;                          // steps of global loads in flight in registers
@@ -50,7 +51,7 @@ constexpr int kMaxGroups = W4_GEMM_MAX_K / kGroup;
 
 // LDS map (bytes).  During the K loop: two activation tiles, two weight
 // tiles, the raw fp16 scales and zeros of the workgroup's rows.  After it:
-// the eight waves' partial sums, over the tiles.
+// the sixteen waves' partial sums, over the tiles.
 constexpr int kXTile = kBM * kGroup * 2;            // 32 KB
 constexpr int kWTile = kBN * kGroup / 2;            // 4 KB
 constexpr int kOffW = 2 * kXTile;
@@ -76,7 +77,7 @@ __device__ __forceinline__ int w_lds(int n, int p) { return (n * 16 + 4 * ((p >>
 constexpr int kXL = kRB * 4 / kWaves;  // activation loads per thread per step
 struct Slot {
     u32x4_t a[kXL];  // activation chunk (tid % 16) of rows tid / 16 + (kThreads / 16) i
-    u32x2_t w;       // weight half-chunk (tid % 8) of row tid / 8
+    uint32_t w;      // weight word (tid % 16) of row tid / 16
 };
 
 // bf16((q_e - z) * s) for the eight codes of one word, k order kept.
@@ -165,20 +166,20 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_mfma_kernel(
     uint32_t xoff[kXL];
 #pragma unroll
     for (int i = 0; i < kXL; ++i) xoff[i] = (uint32_t)(((size_t)min(m0 + xr + kXRows * i, M - 1) * K + 8 * xc) * 2);
-    const int wr = tid >> 3, wc = tid & 7;
-    const uint32_t woff = (uint32_t)min(n0 + wr, N - 1) * row_bytes + 8u * wc;
+    const int wr = tid >> 4, wc = tid & 15;
+    const uint32_t woff = (uint32_t)min(n0 + wr, N - 1) * row_bytes + 4u * wc;
 
     auto issue = [&](int j, Slot& S) {
         const bool live = j < nsteps;
         const uint32_t g = (uint32_t)(g0 + (live ? j : 0));
         const __amdgpu_buffer_rsrc_t ra = live ? rx : rnone;
         const __amdgpu_buffer_rsrc_t rw = live ? rq : rnone;
-        S.w = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rw, (int)woff, (int)sgpr(g * 64u), kAuxNontemporal));
+        S.w = __builtin_amdgcn_raw_buffer_load_b32(rw, (int)woff, (int)sgpr(g * 64u), kAuxNontemporal);
 #pragma unroll
         for (int i = 0; i < kXL; ++i) S.a[i] = buf_load_b128(ra, xoff[i], g * 256u);
     };
     auto store = [&](const Slot& S, int buf) {
-        *reinterpret_cast<u32x2_t*>(lds + kOffW + buf * kWTile + w_lds(wr, 2 * wc)) = S.w;
+        *reinterpret_cast<uint32_t*>(lds + kOffW + buf * kWTile + w_lds(wr, wc)) = S.w;
 #pragma unroll
         for (int i = 0; i < kXL; ++i)
             *reinterpret_cast<u32x4_t*>(lds + buf * kXTile + x_lds(xr + kXRows * i, xc)) = S.a[i];
