@@ -284,6 +284,28 @@ def extra_workloads(w4, host, si, torch, rf):
         del copies
         log(f"prefill M=128 K={K} N={N}: {us:.1f} us, {tf:.0f} TFLOP/s")
 
+    # small-M decode (a few tokens at once) through w4_gemm's small-M path, on the
+    # gate/up and down shapes: weights are read once per call, so the rate is in GB/s
+    small = {}
+    for si_idx, (K, N) in enumerate(si.PREFILL_SHAPES):
+        per = rf.int4_weight_bytes(K, N)
+        n_copies = -(-(512 * MB) // per) + 1
+        copies = [host.int4_tensors(si.int4_linear(102 + si_idx, (c,), K, N)) for c in range(n_copies)]
+        for M in (1, 4, 16):
+            x = host.bf16_tensor(si.bf16_normal(102 + si_idx, (10, M), (M, K)))
+            y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+            g = capture(w4, torch, stream,
+                        lambda: [w4.w4_gemm(x, t["qw"], t["s"], t["z"], y, stream=stream) for t in copies])
+            ms = time_graph(torch, lambda: g.replay(stream), stream, reps=10)
+            us = ms * 1e3 / n_copies
+            gbps = rf.int4_linear_bytes(K, N, M) / (us * 1e-6) / 1e9
+            small[f"m{M}_k{K}_n{N}"] = {"us_per_call": round(us, 2), "GBps": round(gbps, 1),
+                                        "frac_hbm": round(gbps / rf.HBM_PEAK_GBPS, 4)}
+            g.destroy()
+            log(f"small-M GEMM M={M} K={K} N={N}: {us:.1f} us, {gbps:.0f} GB/s")
+        del copies
+    out["small_m_gemm"] = small
+
     # FP4 MoE: FC1 (shared x) then FC2 (one x per slot), a fresh id set per token
     pools = [host.fp4_tensors(p) for p in si.moe_pools()]
     tokens = 64

@@ -296,13 +296,14 @@ int choose_splits(int M, int K, int N) {
 }  // namespace
 
 size_t gemm_int4_workspace_bytes(int M, int K, int N) {
-    if (M <= 0 || N <= 0 || K <= 0 || K % kGroup != 0 || K > W4_GEMM_MAX_K) return 0;
+    if (M <= kGemmSmallMMax || N <= 0 || K <= 0 || K % kGroup != 0 || K > W4_GEMM_MAX_K) return 0;
     const int splits = choose_splits(M, K, N);
     return splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
 hipError_t launch_gemm_int4(const void* x, const int32_t* qw, const void* s, const void* z,
                             void* y, int M, int K, int N, void* workspace, hipStream_t stream) {
+    if (M <= kGemmSmallMMax) return launch_gemm_int4_small_m(x, qw, s, z, y, M, K, N, stream);
     const int splits = choose_splits(M, K, N);
     const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM), (unsigned)splits);
     const uint16_t* xb = static_cast<const uint16_t*>(x);

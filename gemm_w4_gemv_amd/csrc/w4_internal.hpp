@@ -6,12 +6,21 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#ifndef GEMM_SMALL_M_MAX
+#define GEMM_SMALL_M_MAX 32
+#endif
+
 namespace w4 {
 
 hipError_t launch_gemv_int4(const void* x, const int32_t* qw, const void* s, const void* z,
                             void* y, int K, int N, hipStream_t stream);
 
 size_t gemm_int4_workspace_bytes(int M, int K, int N);
+// Small-M path of w4_gemm (M <= kGemmSmallMMax): matrix-core blocks of 16 x
+// rows, weights streamed once per slab of 16 rows, no workspace.
+constexpr int kGemmSmallMMax = GEMM_SMALL_M_MAX;
+hipError_t launch_gemm_int4_small_m(const void* x, const int32_t* qw, const void* s, const void* z,
+                                    void* y, int M, int K, int N, hipStream_t stream);
 hipError_t launch_gemm_int4(const void* x, const int32_t* qw, const void* s, const void* z,
                             void* y, int M, int K, int N, void* workspace, hipStream_t stream);
 
