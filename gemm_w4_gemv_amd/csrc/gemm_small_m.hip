@@ -18,8 +18,11 @@
 //     of one group of row i), so a load instruction reads 16 rows x 64
 //     contiguous bytes.  A 4 x 4 transpose across the four 16-lane rows
 //     (v_permlane32_swap, v_permlane16_swap) leaves word 4t + b in register
-//     t: exactly the B operand of k-slice t (k = 32 t + 8 b .. +7), matching
-//     the A operand that the standard activation load gives.
+//     t: exactly the B operand of k-slice t (k = 32 t + 8 b .. +7).
+//     Activations are loaded 4 rows x 256 bytes per instruction and put in
+//     the matching A layout through a 4 KB LDS tile of the wave's own (an
+//     A-layout load would cover 16 rows x 64 bytes per instruction, measured
+//     15 % slower at M = 16 on the K15360 shape).
 //   * Unpacking uses the bf16 bias trick of the GEMV: 0x4300 | q is exactly
 //     128 + q, 7 integer operations per 8 codes, with the activation pairs
 //     permuted to match.  Per group, sum_k (q - z) s x
@@ -72,8 +75,10 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_small_m_kernel(
     constexpr int kSlots = kCB == 4 ? 3 : 4;  // groups of loads in flight per wave (register budget)
     constexpr int kSZBytes = 2 * kBN * kMaxGroups * 2;    // raw fp16 s then z, [kBN][G] each
     constexpr int kRedBytes = kWaves * kCB * kWave * 16;  // each wave's 16 x kBN partial sums
-    static_assert(kSZBytes + kRedBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
-    __shared__ __attribute__((aligned(16))) char lds[kSZBytes + kRedBytes];
+    constexpr int kXBytes = kWaves * 16 * kGroup * 2;       // each wave's 16 x 128 activation tile
+    constexpr int kTail = kRedBytes > kXBytes ? kRedBytes : kXBytes;
+    static_assert(kSZBytes + kTail <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+    __shared__ __attribute__((aligned(16))) char lds[kSZBytes + kTail];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -95,7 +100,12 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_small_m_kernel(
     uint32_t woff[kCB];
 #pragma unroll
     for (int c = 0; c < kCB; ++c) woff[c] = (uint32_t)min(n0 + 16 * c + li, N - 1) * row_bytes + 16u * lb;
-    const uint32_t aoff = (uint32_t)(((size_t)min(m0 + li, M - 1) * K + 8 * lb) * 2);
+    // Activations: chunk (lane % 16) of rows lane / 16 + 4 i, i.e. 4 rows x
+    // 256 bytes per load instruction; reordered through LDS below.
+    uint32_t aoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) aoff[i] = (uint32_t)(((size_t)min(m0 + (lane >> 4) + 4 * i, M - 1) * K + 8 * li) * 2);
+    char* xw_lds = lds + kSZBytes + wave * (16 * kGroup * 2);
 
     auto issue = [&](int g, Slot<kCB>& S) {
         const bool live = g < g1;
@@ -105,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_small_m_kernel(
 #pragma unroll
         for (int c = 0; c < kCB; ++c) S.w[c] = buf_load_b128<kAuxNontemporal>(rw, woff[c], gg * 64u);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) S.a[t] = buf_load_b128(ra, aoff, gg * 256u + 64u * t);
+        for (int t = 0; t < 4; ++t) S.a[t] = buf_load_b128(ra, aoff[t], gg * 256u);
     };
 
     // The first groups' loads go out before the scale staging below, so
@@ -164,10 +174,18 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_small_m_kernel(
             const int gd = g + d;
             // Activation pairs (x_j, x_{j+4}) of each k-slice, matching the
             // biased weight pairs; the same A against ones gives sum_k x.
+            // Through this wave's LDS tile (row r, chunk c at c ^ r) into the
+            // MFMA layout: lane (i, b) of k-slice t takes chunk 4 t + b of row i.
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int r = (lane >> 4) + 4 * t;
+                *reinterpret_cast<u32x4_t*>(xw_lds + (r * 16 + (li ^ r)) * 16) = S.a[t];
+            }
             u32x4_t a[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const uint32_t xw[4] = {S.a[t].x, S.a[t].y, S.a[t].z, S.a[t].w};
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xw_lds + (li * 16 + ((4 * t + lb) ^ li)) * 16);
+                const uint32_t xw[4] = {v.x, v.y, v.z, v.w};
                 uint32_t p[4];
                 x_pairs_for_biased(xw, p);
                 a[t] = u32x4_t{p[0], p[1], p[2], p[3]};
@@ -201,6 +219,7 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_small_m_kernel(
 
     // Cross-wave sum in wave order.  Lane (i, b) of column block c holds
     // rows 4 b + e, column 16 c + i.
+    __syncthreads();  // every wave is done with its activation tile
     float* red = reinterpret_cast<float*>(lds + kSZBytes);
 #pragma unroll
     for (int c = 0; c < kCB; ++c)
