@@ -46,7 +46,7 @@ FP4_GROUP = 32
 __all__ = [
     "f16_to_f64", "bf16_to_f64", "int4_codes", "dequant_int4", "e2m1_value",
     "fp4_codes", "dequant_fp4", "linear", "gemv_int4", "gemm_int4",
-    "moe_gemv_fp4", "round_bf16", "bf16_bits", "INT4_GROUP", "FP4_GROUP",
+    "moe_gemv_fp4", "moe_gemm_fp4", "round_bf16", "bf16_bits", "INT4_GROUP", "FP4_GROUP",
 ]
 
 
@@ -191,6 +191,33 @@ def moe_gemv_fp4(x_bits, pool_qw, pool_s, ids, rows=None) -> np.ndarray:
         W = dequant_fp4(qw_e, s_e)
         ys.append(linear(bf16_to_f64(x_bits[e])[None, :], W)[0])
     return np.stack(ys)
+
+
+def moe_gemm_fp4(x_bits, row_start, ids, pool_qw, pool_s, cols=None) -> np.ndarray:
+    """FP64 ``y [R, N]`` of a grouped FP4 expert GEMM (several tokens per expert).
+
+    DeepSeek V4 Triton FP4, "深度分析" item 2: the fused FP4 kernel is a
+    matrix product (dequantised tile times a block of activations), and item
+    4: the tokens of a layer are routed to experts, each applying its 2 FC.
+    Group ``e`` owns rows ``row_start[e] .. row_start[e+1] - 1`` of ``x_bits
+    [R, K]`` and applies expert ``ids[e]``: ``y[r] = W_{ids[e]} x[r]``.
+    Rows in no group are NaN.  ``cols`` selects output columns (weight rows).
+    """
+    x = bf16_to_f64(np.atleast_2d(np.asarray(x_bits)))
+    row_start = np.asarray(row_start, dtype=np.int64)
+    ids = np.asarray(ids, dtype=np.int64)
+    pool_qw, pool_s = np.asarray(pool_qw), np.asarray(pool_s)
+    N = pool_qw.shape[1] if cols is None else len(cols)
+    y = np.full((x.shape[0], N), np.nan)
+    for e in range(ids.shape[0]):
+        a, b = int(row_start[e]), int(row_start[e + 1])
+        if a >= b:
+            continue
+        qw_e, s_e = pool_qw[ids[e]], pool_s[ids[e]]
+        if cols is not None:
+            qw_e, s_e = qw_e[cols], s_e[cols]
+        y[a:b] = linear(x[a:b], dequant_fp4(qw_e, s_e))
+    return y
 
 
 # ------------------------------------------------------------------ rounding

@@ -74,6 +74,16 @@ def _moe_ignores_ids(x_bits, pool_qw, pool_s, ids, rows=None):
     return _orig["moe_gemv_fp4"](x_bits, pool_qw, pool_s, list(range(len(ids))), rows)
 
 
+def _moe_gemm_group_shifted(x_bits, row_start, ids, pool_qw, pool_s, cols=None):
+    rs = list(row_start)
+    rs = [rs[0]] + [r + 1 for r in rs[1:-1]] + [rs[-1]]  # every group boundary one row late
+    return _orig["moe_gemm_fp4"](x_bits, rs, ids, pool_qw, pool_s, cols)
+
+
+def _moe_gemm_ids_ignored(x_bits, row_start, ids, pool_qw, pool_s, cols=None):
+    return _orig["moe_gemm_fp4"](x_bits, row_start, list(range(len(ids))), pool_qw, pool_s, cols)
+
+
 def _dequant_fp4_scale_by_k(qw, s_bits, group=32):
     v = oracle.e2m1_value(oracle.fp4_codes(qw))
     s = oracle.bf16_to_f64(s_bits)
@@ -93,6 +103,8 @@ MUTANTS = {
     "bf16_round_half_up": ("round_bf16", _round_half_up),
     "moe_slot_ids_ignored": ("moe_gemv_fp4", _moe_ignores_ids),
     "fp4_group_of_16": ("dequant_fp4", _dequant_fp4_scale_by_k),
+    "moe_gemm_group_boundary_off_by_one": ("moe_gemm_fp4", _moe_gemm_group_shifted),
+    "moe_gemm_ids_ignored": ("moe_gemm_fp4", _moe_gemm_ids_ignored),
 }
 
 

@@ -217,6 +217,49 @@ def test_moe_slot_order_and_broadcast():
     assert np.array_equal(y, y2)
 
 
+def test_moe_gemm_groups_by_hand():
+    """Grouped FP4 GEMM on a hand-built case: group 0 = rows 0, 1 -> expert 1;
+    group 1 = no rows; group 2 = row 2 -> expert 0.  One-hot rows pick single
+    weights, whose values follow from the OCP E2M1 table times the scale."""
+    table = {int(k): v for k, v in load("fp4_e2m1.json")["table"].items()}
+    K, N = 32, 2
+    codes = np.zeros((2, N, K), dtype=np.uint8)
+    codes[0, :, 5] = [3, 12]     # expert 0, k = 5: 1.5, -2.0
+    codes[1, :, 0] = [7, 1]      # expert 1, k = 0: 6.0, 0.5
+    codes[1, :, 31] = [10, 4]    # expert 1, k = 31: -1.0, 2.0
+    pool = pack_fp4(codes)
+    s = bf16_bits_exact(np.array([[[0.5]] * N, [[4.0]] * N], dtype=np.float32))
+    x = np.zeros((3, K), dtype=np.float32)
+    x[0, 0] = 1.0
+    x[1, 31] = 1.0
+    x[2, 5] = 1.0
+    y = oracle.moe_gemm_fp4(bf16_bits_exact(x), [0, 2, 2, 3], [1, 1, 0], pool, s)
+    expect = [[table[7] * 4.0, table[1] * 4.0],
+              [table[10] * 4.0, table[4] * 4.0],
+              [table[3] * 0.5, table[12] * 0.5]]
+    assert y.tolist() == expect == [[24.0, 2.0], [-4.0, 8.0], [0.75, -1.0]]
+
+
+def test_moe_gemm_rows_match_per_token_gemv():
+    """Every row of the grouped GEMM equals the M = 1 expert GEMV of its token
+    with its group's expert; rows outside every group stay NaN."""
+    g = rng(4, 7)
+    P, N, K = 5, 6, 96
+    pool = g.integers(0, 256, size=(P, N, K // 2)).astype(np.uint8)
+    s = bf16_bits_exact((np.exp2(g.integers(-8, -1, size=(P, N, K // 32)))
+                         * g.choice([1.0, 1.25, 1.5, 1.75], size=(P, N, K // 32))).astype(np.float32))
+    R = 9
+    x = bf16_normal(4, (7, 1), (R, K))
+    row_start, ids = [0, 3, 3, 7, 8], [4, 1, 0, 2]   # row 8 in no group
+    y = oracle.moe_gemm_fp4(x, row_start, ids, pool, s)
+    for e, expert in enumerate(ids):
+        for r in range(row_start[e], row_start[e + 1]):
+            assert np.allclose(y[r], oracle.moe_gemv_fp4(x[r], pool, s, [expert])[0], rtol=1e-12, atol=1e-300)
+    assert np.all(np.isnan(y[8]))
+    cols = [5, 0, 3]
+    assert np.array_equal(oracle.moe_gemm_fp4(x, row_start, ids, pool, s, cols=cols)[:8], y[:8][:, cols])
+
+
 # ------------------------------------------------------------ brute force
 @pytest.mark.parametrize("K,N,M", [(128, 1, 1), (128, 3, 2), (256, 2, 2), (256, 3, 1)])
 def test_bruteforce_exact_fractions_int4(K, N, M):
