@@ -21,7 +21,7 @@ import torch
 
 __all__ = [
     "W4Error", "lib", "LIB_PATH", "w4_abi_version", "w4_status_string", "w4_last_error",
-    "w4_gemv", "w4_gemm", "w4_gemm_workspace_bytes", "w4_moe_gemv",
+    "w4_gemv", "w4_gemm", "w4_gemm_workspace_bytes", "w4_moe_gemv", "w4_moe_gemm",
     "w4_graph_begin", "w4_graph_end", "w4_graph_replay", "w4_graph_destroy", "W4Graph",
     "w4_dequant_int4", "w4_dequant_fp4", "INT4_GROUP", "FP4_GROUP", "GEMV_MAX_K",
     "GemvDesc", "W4Chain", "w4_chain_workspace_bytes", "w4_chain_create", "w4_chain_run",
@@ -60,6 +60,7 @@ SIGNATURES = {
     "w4_gemm_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "w4_gemm": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "w4_moe_gemv": (_i32, [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "w4_moe_gemm": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "w4_graph_begin": (_i32, [_vp]),
     "w4_graph_end": (_i32, [_vp, ctypes.POINTER(_vp)]),
     "w4_graph_replay": (_i32, [_vp, _vp]),
@@ -185,6 +186,29 @@ def w4_gemm(x, qw, s, z, y, workspace=None, group: int = INT4_GROUP, stream=None
         pw, nbytes = _dev(workspace, "workspace", (workspace.dtype,)), workspace.numel() * workspace.element_size()
     _check(lib.w4_gemm(_dev(x, "x", _BF16), pq, ps, pz, _dev(y, "y", _BF16), M, K, N, group, pw, nbytes,
                        _stream(stream)), "w4_gemm")
+    return y
+
+
+def w4_moe_gemm(x, row_start, expert_ids, qw_fp4, s_fp4, y, max_rows: int, stream=None) -> torch.Tensor:
+    """Group ``e`` applies FP4 expert ``expert_ids[e]`` to rows ``row_start[e] .. row_start[e+1]-1`` of ``x``."""
+    if qw_fp4.dim() != 3:
+        raise ValueError("qw_fp4 must be [experts, N, K/2]")
+    num_experts, N, half_k = qw_fp4.shape
+    K = 2 * half_k
+    if tuple(s_fp4.shape) != (num_experts, N, K // FP4_GROUP):
+        raise ValueError(f"s_fp4 must be [experts, N, K/32]; got {tuple(s_fp4.shape)}")
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [R, K] with K = {K}; got {tuple(x.shape)}")
+    R = x.shape[0]
+    E = expert_ids.numel()
+    if row_start.numel() != E + 1:
+        raise ValueError(f"row_start must have E + 1 = {E + 1} entries")
+    if tuple(y.shape) != (R, N):
+        raise ValueError(f"y must be [R, N] = {(R, N)}; got {tuple(y.shape)}")
+    _check(lib.w4_moe_gemm(_dev(x, "x", _BF16), _dev(row_start, "row_start", _I32),
+                           _dev(expert_ids, "expert_ids", _I32), _dev(qw_fp4, "qw_fp4", _U8),
+                           _dev(s_fp4, "s_fp4", _BF16), _dev(y, "y", _BF16), R, E, int(max_rows), num_experts, K, N,
+                           _stream(stream)), "w4_moe_gemm")
     return y
 
 

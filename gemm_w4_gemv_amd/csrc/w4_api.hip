@@ -164,6 +164,38 @@ W4_API w4_status w4_moe_gemv(const void* x, int64_t x_stride, const uint8_t* qw_
     return err == hipSuccess ? W4_OK : hip_fail(err, fn);
 }
 
+W4_API w4_status w4_moe_gemm(const void* x, const int32_t* row_start, const int32_t* expert_ids,
+                             const uint8_t* qw_fp4, const void* s_fp4, void* y, int R, int E, int max_rows,
+                             int num_experts, int K, int N, void* stream) {
+    const char* fn = "w4_moe_gemm";
+    if (!x || !row_start || !expert_ids || !qw_fp4 || !s_fp4 || !y)
+        return fail(W4_ERR_NULL, "%s: x, row_start, expert_ids, qw_fp4, s_fp4 and y must not be NULL", fn);
+    if (R < 0 || E < 0 || max_rows < 0 || N < 0)
+        return fail(W4_ERR_SHAPE, "%s: R = %d, E = %d, max_rows = %d, N = %d must not be negative", fn, R, E,
+                    max_rows, N);
+    if (K <= 0 || K % 128 != 0 || K > W4_MOE_GEMM_MAX_K)
+        return fail(W4_ERR_SHAPE, "%s: K = %d must be a positive multiple of 128 up to %d", fn, K,
+                    W4_MOE_GEMM_MAX_K);
+    if (num_experts < 1) return fail(W4_ERR_ARG, "%s: num_experts = %d must be positive", fn, num_experts);
+    if ((unsigned long long)N * (unsigned long long)(K / 2) > W4_GEMV_MAX_MATRIX_BYTES ||
+        (unsigned long long)R * (unsigned long long)K * 2ull > W4_GEMV_MAX_MATRIX_BYTES)
+        return fail(W4_ERR_SHAPE, "%s: N * K / 2 or R * K * 2 exceeds %llu bytes", fn, W4_GEMV_MAX_MATRIX_BYTES);
+    if (!aligned(x, 16) || !aligned(qw_fp4, 16))
+        return fail(W4_ERR_ALIGN, "%s: x and qw_fp4 must be 16-byte aligned", fn);
+    if (!aligned(s_fp4, 8) || !aligned(y, 2) || !aligned(row_start, 4) || !aligned(expert_ids, 4))
+        return fail(W4_ERR_ALIGN, "%s: s_fp4 must be 8-byte, y 2-byte, row_start and expert_ids 4-byte aligned", fn);
+    const Range ry = range(y, (size_t)R * N * 2);
+    const Range ins[5] = {range(x, (size_t)R * K * 2), range(qw_fp4, (size_t)num_experts * N * K / 2),
+                          range(s_fp4, (size_t)num_experts * N * (K / 32) * 2), range(expert_ids, (size_t)E * 4),
+                          range(row_start, (size_t)(E + 1) * 4)};
+    for (const Range& r : ins)
+        if (overlap(ry, r)) return fail(W4_ERR_ALIAS, "%s: y overlaps an input", fn);
+    if (R == 0 || E == 0 || max_rows == 0 || N == 0) return W4_OK;
+    hipError_t err = w4::launch_moe_gemm_fp4(x, row_start, expert_ids, qw_fp4, s_fp4, y, R, E, max_rows, num_experts,
+                                             K, N, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4_OK : hip_fail(err, fn);
+}
+
 struct w4_graph {
     hipGraph_t graph;
     hipGraphExec_t exec;

@@ -28,6 +28,10 @@ hipError_t launch_moe_gemv_fp4(const void* x, int64_t x_stride, const uint8_t* q
                                const void* s, const int32_t* ids, void* y, int E,
                                int num_experts, int K, int N, hipStream_t stream);
 
+hipError_t launch_moe_gemm_fp4(const void* x, const int32_t* row_start, const int32_t* ids, const uint8_t* qw,
+                               const void* s, void* y, int R, int E, int max_rows, int num_experts, int K, int N,
+                               hipStream_t stream);
+
 hipError_t launch_dequant_int4(const int32_t* qw, const void* s, const void* z, float* out_f32,
                                void* out_bf16, int K, int N, hipStream_t stream);
 hipError_t launch_dequant_fp4(const uint8_t* qw, const void* s, float* out_f32, void* out_bf16,

@@ -85,6 +85,9 @@ typedef enum w4_status {
  * (M * K * 2 bytes) and the packed weights (N * K / 2 bytes) of one call must
  * each stay within W4_GEMV_MAX_MATRIX_BYTES: 32-bit offsets address them. */
 #define W4_GEMM_MAX_K 32768
+/* Largest K accepted by w4_moe_gemm (a workgroup stages the scales of its
+ * weight rows, all K / 32 groups, in LDS). */
+#define W4_MOE_GEMM_MAX_K 8192
 #define W4_INT4_GROUP 128
 #define W4_FP4_GROUP 32
 
@@ -154,6 +157,37 @@ W4_API w4_status w4_gemm(const void* x, const int32_t* qw, const void* s, const 
 W4_API w4_status w4_moe_gemv(const void* x, int64_t x_stride, const uint8_t* qw_fp4,
                              const void* s_fp4, const int32_t* expert_ids, void* y,
                              int E, int num_experts, int K, int N, void* stream);
+
+/*
+ * w4_moe_gemm -- grouped FP4 expert GEMM: several tokens per expert (MoE
+ * prefill, or a decode batch routed to experts).
+ *   for each group e < E, rows r in [row_start[e], row_start[e+1]):
+ *   y[r][n] = bf16( sum_k e2m1(c[ids[e]][n][k]) * s[ids[e]][n][k/32] * x[r][k] )
+ * "DeepSeek V4 Triton FP4 优化实战", "深度分析" items 2 (the fused FP4 kernel
+ * is a matrix product; even k in the low nibble, odd k in the high nibble)
+ * and 4 (tokens routed to experts).  The FP4 codes are decoded in registers
+ * straight into the matrix-core operand; each group of 32 k is summed
+ * exactly in FP32 and scaled in FP32.
+ *   x          device bf16 [R][K], 16-byte aligned
+ *   row_start  device int32 [E+1], 4-byte aligned (read on the device):
+ *              group e owns rows row_start[e] .. row_start[e+1] - 1;
+ *              values are clamped into [0, R] and a group's end below its
+ *              start counts as empty
+ *   expert_ids device int32 [E], 4-byte aligned (read on the device); an id
+ *              outside [0, num_experts) makes that group's rows NaN
+ *   qw_fp4     device uint8 [num_experts][N][K/2], 16-byte aligned
+ *   s_fp4      device bf16 [num_experts][N][K/32], 8-byte aligned
+ *   y          device bf16 [R][N], 2-byte aligned; rows in no group are not
+ *              written
+ *   max_rows   the most rows any group has: rows of a group past its first
+ *              max_rows are not written (precondition, not checked)
+ *   K multiple of 128, 0 < K <= W4_MOE_GEMM_MAX_K;  R, E, max_rows, N >= 0;
+ *   num_experts >= 1;  N * K / 2 and R * K * 2 <= W4_GEMV_MAX_MATRIX_BYTES.
+ * Errors: W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_ALIAS, W4_ERR_ARG, W4_ERR_HIP.
+ */
+W4_API w4_status w4_moe_gemm(const void* x, const int32_t* row_start, const int32_t* expert_ids,
+                             const uint8_t* qw_fp4, const void* s_fp4, void* y, int R, int E,
+                             int max_rows, int num_experts, int K, int N, void* stream);
 
 /*
  * Decode-step graphs.  "Lab 5: Gemma4 端到端推理优化", section "CUDA Graph":

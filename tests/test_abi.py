@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for name in names:
         assert hasattr(lib, name), f"libw4.so does not export {name}"
         assert name in w4.SIGNATURES, f"binding has no signature for {name}"
@@ -117,6 +117,30 @@ def test_moe_validation():
     assert call(ids=IDS + 2) == ALIGN
     assert call(y=IDS) == ALIAS
     assert call(E=0) == OK
+
+
+def test_moe_gemm_validation():
+    RS = IDS + 0x1000
+
+    def call(**k):
+        return lib.w4_moe_gemm(k.get("x", X), k.get("rs", RS), k.get("ids", IDS), k.get("qw", QW), k.get("s", S),
+                               k.get("y", Y), k.get("R", 96), k.get("E", 6), k.get("mr", 16), k.get("ne", 64),
+                               k.get("K", 4096), k.get("N", 2048), None)
+    assert call(rs=None) == NULL
+    assert call(ids=None) == NULL
+    assert call(ne=0) == ARG
+    assert call(K=4096 + 32) == SHAPE          # not a multiple of 128
+    assert call(K=8192 + 128) == SHAPE         # past W4_MOE_GEMM_MAX_K
+    assert call(R=-1) == SHAPE
+    assert call(mr=-1) == SHAPE
+    assert call(R=(1 << 31) // 4096) == SHAPE  # activations past 32-bit offsets
+    assert call(qw=QW + 8) == ALIGN
+    assert call(s=S + 4) == ALIGN              # scales need 8-byte alignment
+    assert call(rs=RS + 2) == ALIGN
+    assert call(y=RS) == ALIAS
+    assert call(y=X + 64) == ALIAS
+    assert call(E=0) == OK and call(R=0) == OK and call(mr=0) == OK and call(N=0) == OK
+    assert "w4_moe_gemm" in w4.w4_last_error()
 
 
 def test_graph_and_dequant_validation():

@@ -604,3 +604,66 @@ def test_read_probe_reads_every_word():
         got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
         want = np.bitwise_xor.reduce(words.numpy().view(np.uint32))
         assert got == want, f"{nbytes} bytes"
+
+
+# ------------------------------------------------------- FP4 grouped expert GEMM
+def run_moe_gemm(dev_pool, x_bits, row_start, ids, max_rows, fill=None):
+    R, _ = x_bits.shape
+    N = dev_pool["qw"].shape[1]
+    y = torch.empty(R, N, dtype=torch.bfloat16, device=DEV)
+    if fill is not None:
+        y.view(torch.int16).fill_(fill)
+    w4.w4_moe_gemm(host.bf16_tensor(x_bits), torch.tensor(row_start, dtype=torch.int32, device=DEV),
+                   torch.tensor(ids, dtype=torch.int32, device=DEV), dev_pool["qw"], dev_pool["s"], y, max_rows)
+    torch.cuda.synchronize()
+    return y
+
+
+def check_moe_groups(y, x_bits, pool, row_start, ids, cols=None):
+    y_ref = oracle.moe_gemm_fp4(x_bits, row_start, ids, pool["qw"], pool["s"], cols=cols)
+    for e, expert in enumerate(ids):
+        a, b = row_start[e], row_start[e + 1]
+        if a >= b:
+            continue
+        qw_e, s_e = pool["qw"][expert], pool["s"][expert]
+        if cols is not None:
+            qw_e, s_e = qw_e[cols], s_e[cols]
+        wmax = np.abs(oracle.dequant_fp4(qw_e, s_e)).max(axis=1)
+        check_outputs(y[a:b], y_ref[a:b], xnorm(x_bits[a:b]), wmax, f"moe_gemm group {e} (expert {expert})")
+
+
+@pytest.mark.parametrize("fc", [0, 1])
+def test_moe_gemm_prefill_groups(fc):
+    """Both FC shapes of the 64-expert pools: 6 groups of 3, 0, 16, 5, 1 and 9 rows
+    (one empty, one full slab); every output of FC1, 512 sampled columns of FC2."""
+    K, N = si.MOE_FC[fc]
+    pool = si.moe_pools()[fc]
+    dev_pool = host.fp4_tensors(pool)
+    sizes = [3, 0, 16, 5, 1, 9]
+    row_start = np.concatenate([[0], np.cumsum(sizes)]).tolist()
+    ids = si.expert_ids(si.SEED, (50, fc)).tolist()
+    x = si.bf16_normal(si.SEED, (50, fc, 7), (row_start[-1], K))
+    print(f"moe_gemm fc={fc} K={K} N={N} rows={sizes} ids={ids}", flush=True)
+    y = host.bf16_values(run_moe_gemm(dev_pool, x, row_start, ids, max(sizes)))
+    cols = None if fc == 0 else np.sort(np.random.default_rng(5).choice(N, 512, replace=False))
+    check_moe_groups(y if cols is None else y[:, cols], x, pool, row_start, ids, cols)
+
+
+def test_moe_gemm_multi_slab_invalid_id_and_untouched_rows():
+    """Groups of 40 and 17 rows (three and two slabs of 16), an id outside the pool
+    (its rows NaN), rows in no group left as they were; run twice, same bits."""
+    P, K, N = 8, 384, 100
+    pool = si.fp4_pool(51, (1,), P, K, N)
+    dev_pool = host.fp4_tensors(pool)
+    row_start = [0, 40, 40, 57, 60]          # groups: 40 rows, empty, 17 rows, 3 rows (bad id); rows 60, 61 in none
+    ids = [6, 2, 1, 9]
+    x = si.bf16_normal(51, (2,), (62, K))
+    print("moe_gemm multi-slab", flush=True)
+    y1 = run_moe_gemm(dev_pool, x, row_start, ids, 40, fill=0x1234)
+    y2 = run_moe_gemm(dev_pool, x, row_start, ids, 40, fill=0x1234)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    bits = host.bits_of(y1)
+    assert np.all(bits[60:] == 0x1234)
+    yv = host.bf16_values(y1)
+    assert np.all(np.isnan(yv[57:60]))
+    check_moe_groups(yv, x, pool, row_start[:4], ids[:3])
