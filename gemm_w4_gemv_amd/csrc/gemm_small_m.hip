@@ -1,4 +1,4 @@
-// Small-M INT4 GEMM (a few decode tokens at once, M <= 16 per slab of rows):
+// Small-M INT4 GEMM (a few decode tokens at once, M <= 16):
 // y[m][n] = bf16( sum_k (q[n][k] - z) s x[m][k] ).
 //
 // "Lab 5: Gemma4 端到端推理优化": decode (one token) and prefill (many) run
@@ -10,7 +10,7 @@
 //
 // gfx950 design:
 //   * A workgroup owns 64, 32 or 16 weight rows (1 to 4 MFMA column blocks;
-//     the widest that still launches 240 workgroups) and one slab of 16 x
+//     the widest that still launches 240 workgroups) and all M (<= 16) x
 //     rows; its 8 waves split the K groups, each streaming its own groups
 //     with three or four groups of loads in flight and no barrier inside
 //     the K loop.
@@ -67,7 +67,7 @@ struct Slot {
 };
 
 // kCB column blocks of 16 weight rows per workgroup.
-template <int kCB, bool kMultiSlab>
+template <int kCB>
 __global__ __launch_bounds__(kThreads) void gemm_int4_small_m_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ s,
     const uint16_t* __restrict__ z, uint16_t* __restrict__ y, int M, int K, int N) {
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_small_m_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int li = lane & 15, lb = lane >> 4;
     const int n0 = blockIdx.x * kBN;
-    const int m0 = kMultiSlab ? blockIdx.y * 16 : 0;
+    constexpr int m0 = 0;
     const int G = K / kGroup;
     const int g0 = (int)(((long)wave * G) / kWaves);
     const int g1 = (int)(((long)(wave + 1) * G) / kWaves);
@@ -250,22 +250,16 @@ hipError_t launch_gemm_int4_small_m(const void* x, const int32_t* qw, const void
     const uint16_t* sb = static_cast<const uint16_t*>(s);
     const uint16_t* zb = static_cast<const uint16_t*>(z);
     uint16_t* yb = static_cast<uint16_t*>(y);
-    const unsigned slabs = (unsigned)((M + 15) / 16);
     // The widest tile (64, 32 or 16 weight rows) that still gives at least
     // 240 workgroups: wider tiles read the activations fewer times.
     auto launch = [&](auto cb) {
         constexpr int kCB = decltype(cb)::value;
-        const dim3 grid((unsigned)((N + 16 * kCB - 1) / (16 * kCB)), slabs);
-        if (slabs == 1)
-            gemm_int4_small_m_kernel<kCB, false><<<grid, kThreads, 0, stream>>>(xb, wb, sb, zb, yb, M, K, N);
-        else
-            gemm_int4_small_m_kernel<kCB, true><<<grid, kThreads, 0, stream>>>(xb, wb, sb, zb, yb, M, K, N);
+        const dim3 grid((unsigned)((N + 16 * kCB - 1) / (16 * kCB)));
+        gemm_int4_small_m_kernel<kCB><<<grid, kThreads, 0, stream>>>(xb, wb, sb, zb, yb, M, K, N);
         return hipGetLastError();
     };
-    const long tiles64 = (long)((N + 63) / 64) * slabs;
-    const long tiles32 = (long)((N + 31) / 32) * slabs;
-    if (tiles64 >= 240) return launch(std::integral_constant<int, 4>{});
-    if (tiles32 >= 240) return launch(std::integral_constant<int, 2>{});
+    if ((N + 63) / 64 >= 240) return launch(std::integral_constant<int, 4>{});
+    if ((N + 31) / 32 >= 240) return launch(std::integral_constant<int, 2>{});
     return launch(std::integral_constant<int, 1>{});
 }
 

@@ -122,10 +122,10 @@ W4_API w4_status w4_gemv(const void* x, const int32_t* qw, const void* s, const 
  * dequantised BF16 weights into a tensor-core GEMM) and "INT4 融合 GEMV"
  * (equivalence tested at M = 128).  Here each packed word is dequantised in
  * registers straight into the matrix-core operand (BF16, round-to-nearest-
- * even) and the BF16 weight is never written to device memory.  M <= 32 (a
- * few decode tokens at once) takes a streaming path instead: slabs of 16 x
- * rows against the exact codes, the group's zero and scale applied to the
- * FP32 block sums, weights read once per slab and no workspace.
+ * even) and the BF16 weight is never written to device memory.  M <= 16 (a
+ * few decode tokens at once) takes a streaming path instead: one 16-row
+ * matrix-core block of x against the exact codes, the group's zero and scale
+ * applied to the FP32 block sums, weights read once and no workspace.
  *   x   device bf16 [M][K], 16-byte aligned   qw, s, z as for w4_gemv
  *   y   device bf16 [M][N], 2-byte aligned
  *   workspace  device memory of at least w4_gemm_workspace_bytes(M, K, N, g)

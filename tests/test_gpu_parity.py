@@ -238,9 +238,9 @@ def test_gemm_parity(M, K, N):
     check_outputs(y, y_ref, xnorm(x), wmax, f"gemm M={M} K={K} N={N}")
 
 
-@pytest.mark.parametrize("M", [32, 128])
+@pytest.mark.parametrize("M", [16, 128])
 def test_gemm_deterministic(M):
-    """Both paths (small-M slabs at M = 32, the tiled GEMM with split K at M = 128)."""
+    """Both paths (the small-M path at M = 16, the tiled GEMM with split K at M = 128)."""
     lin, x_bits = si.prefill(1, M=M)
     a, _ = run_gemm(lin, x_bits)
     b, _ = run_gemm(lin, x_bits)
@@ -248,15 +248,15 @@ def test_gemm_deterministic(M):
 
 
 @pytest.mark.parametrize("M,K,N", [
-    (2, 3840, 15360),    # one slab, 64-row tiles (the gate / up shape)
-    (8, 15360, 3840),    # one slab, 16-row tiles, 15 groups per wave (the down shape)
-    (24, 1024, 3840),    # two slabs, 32-row tiles
+    (2, 3840, 15360),    # 64-row tiles (the gate / up shape)
+    (8, 15360, 3840),    # 16-row tiles, 15 groups per wave (the down shape)
+    (16, 1024, 7680),    # 32-row tiles, all 16 rows
     (13, 640, 1000),     # 5 groups for 8 waves (some waves idle), ragged N
-    (32, 256, 130),      # two slabs, 2 groups
+    (16, 256, 130),      # 2 groups
     (3, 4096, 262144),   # logits-sized N, 64-row tiles
 ])
 def test_gemm_small_m(M, K, N):
-    """The small-M path of w4_gemm (M <= 32): sampled rows against the oracle."""
+    """The small-M path of w4_gemm (M <= 16): sampled rows against the oracle."""
     print(f"gemm small M={M} K={K} N={N}", flush=True)
     lin = si.int4_linear(23, (M, K, N), K, N)
     x = si.bf16_normal(23, (M, K, N, 7), (M, K))
@@ -266,6 +266,18 @@ def test_gemm_small_m(M, K, N):
     rows = np.unique(np.concatenate([[0, N - 1], np.arange(min(N, 96)), g.choice(N, min(N, 160), replace=False)]))
     y_ref, wmax = int4_ref(lin, x, rows)
     check_outputs(y[:, rows], y_ref, xnorm(x), wmax, f"gemm small M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("M", [17, 32])
+def test_gemm_just_past_small_m(M):
+    """M = 17 and 32 take the tiled GEMM (split K on this shape): every output."""
+    K, N = 1024, 3840
+    lin = si.int4_linear(24, (M,), K, N)
+    x = si.bf16_normal(24, (M, 7), (M, K))
+    assert w4.w4_gemm_workspace_bytes(M, K, N) > 0
+    y, split = run_gemm(lin, x)
+    y_ref, wmax = int4_ref(lin, x)
+    check_outputs(y, y_ref, xnorm(x), wmax, f"gemm M={M} K={K} N={N}")
 
 
 # ------------------------------------------------------------------- FP4 MoE
