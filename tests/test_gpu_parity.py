@@ -679,3 +679,18 @@ def test_moe_gemm_multi_slab_invalid_id_and_untouched_rows():
     yv = host.bf16_values(y1)
     assert np.all(np.isnan(yv[57:60]))
     check_moe_groups(yv, x, pool, row_start[:4], ids[:3])
+
+
+def test_moe_gemm_row_table_clamped():
+    """Group bounds outside [0, R] are clamped on the device: a start below 0 reads
+    as 0, an end past R as R, and an end below its start as an empty group."""
+    P, K, N = 4, 256, 48
+    pool = si.fp4_pool(52, (1,), P, K, N)
+    dev_pool = host.fp4_tensors(pool)
+    R = 20
+    x = si.bf16_normal(52, (2,), (R, K))
+    print("moe_gemm clamped row table", flush=True)
+    y = run_moe_gemm(dev_pool, x, [-5, 6, 6, 1000, 3], [3, 1, 0, 2], 16, fill=0x1234)
+    yv = host.bf16_values(y)
+    # effective groups: rows 0..5 -> expert 3; empty; rows 6..19 -> expert 0; empty (end below start)
+    check_moe_groups(yv, x, pool, [0, 6, 6, 20], [3, 1, 0])
