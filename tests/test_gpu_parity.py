@@ -694,3 +694,54 @@ def test_moe_gemm_row_table_clamped():
     yv = host.bf16_values(y)
     # effective groups: rows 0..5 -> expert 3; empty; rows 6..19 -> expert 0; empty (end below start)
     check_moe_groups(yv, x, pool, [0, 6, 6, 20], [3, 1, 0])
+
+
+def test_graph_replays_of_gemm_paths_equal_eager():
+    """The tiled GEMM (split K), the small-M GEMM and the grouped FP4 GEMM captured
+    in one HIP graph: five replays, with eager work and synchronisations between
+    them and the outputs cleared before each, all equal the eager results bit for bit."""
+    stream = torch.cuda.Stream()
+    lin = si.int4_linear(25, (1,), 2048, 192)
+    t = host.int4_tensors(lin)
+    xb = host.bf16_tensor(si.bf16_normal(25, (2,), (128, 2048)))
+    xs = host.bf16_tensor(si.bf16_normal(25, (3,), (5, 2048)))
+    yb = torch.empty(128, 192, dtype=torch.bfloat16, device=DEV)
+    ys = torch.empty(5, 192, dtype=torch.bfloat16, device=DEV)
+    nbytes = w4.w4_gemm_workspace_bytes(128, 2048, 192)
+    assert nbytes > 0
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device=DEV)
+    pool = host.fp4_tensors(si.fp4_pool(25, (4,), 6, 512, 80))
+    xm = host.bf16_tensor(si.bf16_normal(25, (5,), (30, 512)))
+    ym = torch.empty(30, 80, dtype=torch.bfloat16, device=DEV)
+    rs = torch.tensor([0, 7, 7, 23, 30], dtype=torch.int32, device=DEV)
+    ids = torch.tensor([5, 0, 2, 3], dtype=torch.int32, device=DEV)
+
+    def body():
+        w4.w4_gemm(xb, t["qw"], t["s"], t["z"], yb, workspace=ws, stream=stream)
+        w4.w4_gemm(xs, t["qw"], t["s"], t["z"], ys, stream=stream)
+        w4.w4_moe_gemm(xm, rs, ids, pool["qw"], pool["s"], ym, 16, stream=stream)
+
+    with torch.cuda.stream(stream):
+        body()
+    stream.synchronize()
+    ref = [y.clone() for y in (yb, ys, ym)]
+    torch.cuda.synchronize()
+    w4.w4_graph_begin(stream)
+    try:
+        body()
+    finally:
+        g = w4.w4_graph_end(stream)
+    try:
+        for rep in range(5):
+            for y in (yb, ys, ym):
+                y.zero_()
+            torch.cuda.synchronize()
+            g.replay(stream)
+            stream.synchronize()
+            for y, r in zip((yb, ys, ym), ref):
+                assert torch.equal(y.view(torch.int16), r.view(torch.int16)), f"replay {rep}"
+            junk = torch.randn(1 << 20, device=DEV) * 2  # unrelated eager work between replays
+            torch.cuda.synchronize()
+            del junk
+    finally:
+        g.destroy()
