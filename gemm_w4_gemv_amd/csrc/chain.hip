@@ -529,7 +529,15 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainStage* 
     __syncthreads();
     if (wave >= 1 && wave <= kChainComputeWaves) {
         const int W = L.workers * kChainComputeWaves;
-        compute_wave(L, sh, xl, lane, wave - 1, uniform((int)blockIdx.x * kChainComputeWaves + (wave - 1)), W);
+        // Position of this compute wave among the workgroup's in the stage
+        // split.  Waves are placed on the 4 SIMDs in turn (wave w on SIMD
+        // w % 4), so compute waves 1..8 sit two per SIMD; numbering them
+        // 2 * SIMD + (first or second on it) makes the busy waves of a stage
+        // with fewer tiles than waves (every second one, every fourth one)
+        // land on different SIMDs instead of sharing two.  Any numbering is
+        // correct; this one only spreads the work.
+        const int l = 2 * (wave % 4) + (wave - 1) / 4;
+        compute_wave(L, sh, xl, lane, wave - 1, uniform((int)blockIdx.x * kChainComputeWaves + l), W);
     } else {
         staging_wave(L, sh, xl, lane, wave == 0 ? 0 : wave - kChainComputeWaves);
     }
