@@ -745,3 +745,29 @@ def test_graph_replays_of_gemm_paths_equal_eager():
             del junk
     finally:
         g.destroy()
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (128, 32768, 64),    # the largest K: scales and zeros of 256 groups staged in LDS, K split
+    (4, 32768, 80),      # the same K through the small-M path
+    (130, 32768, 70),    # two row tiles, ragged N
+])
+def test_gemm_max_k(M, K, N):
+    print(f"gemm max K M={M} K={K} N={N}", flush=True)
+    lin = si.int4_linear(26, (M, K, N), K, N)
+    x = si.bf16_normal(26, (M, K, N, 7), (M, K))
+    y, _ = run_gemm(lin, x)
+    y_ref, wmax = int4_ref(lin, x)
+    check_outputs(y, y_ref, xnorm(x), wmax, f"gemm M={M} K={K} N={N}")
+
+
+def test_moe_gemm_max_k():
+    """The largest K of w4_moe_gemm (8192: scales of 256 groups per row staged in LDS)."""
+    P, K, N = 3, 8192, 40
+    pool = si.fp4_pool(53, (1,), P, K, N)
+    dev_pool = host.fp4_tensors(pool)
+    x = si.bf16_normal(53, (2,), (21, K))
+    row_start, ids = [0, 9, 21], [2, 0]
+    print("moe_gemm max K", flush=True)
+    y = host.bf16_values(run_moe_gemm(dev_pool, x, row_start, ids, 12))
+    check_moe_groups(y, x, pool, row_start, ids)
