@@ -39,6 +39,7 @@ Also reported, outside the timed step:
 
     python bench.py [--steps K] [--warmup W] [--no-extra] [--no-cpu-baseline]
     python bench.py --counters   # only the kernels that HBM counters are read for
+    python bench.py --gemm-calls # only w4_gemm at M = 128 and M = 16 on the two decode shapes, 5 calls each
 
 ``--counters`` runs five chain-kernel launches of the (timed, linked) decode step, then five
 copies of 512 MiB by torch (a plain copy of known size, read once and
@@ -78,6 +79,9 @@ def parse():
     p.add_argument("--cpu-layers", type=int, default=12, help="decode layers the oracle sample covers")
     p.add_argument("--counters", action="store_true",
                    help="run only five chain launches and five 512 MiB copies (for HBM counter runs)")
+    p.add_argument("--gemm-calls", action="store_true",
+                   help="run only w4_gemm at M = 128 and M = 16 on the two decode shapes, five calls each "
+                        "(for kernel traces and SQ counter runs of the GEMM kernels)")
     return p.parse_args()
 
 
@@ -424,6 +428,23 @@ def counter_run(torch, host, si) -> int:
     return 1 if err else 0
 
 
+def gemm_calls(w4, torch, host, si) -> int:
+    """w4_gemm at M = 128 (the tiled kernel; K15360 -> N3840 splits K) and M = 16
+    (the small-M kernel) on the two decode shapes, five calls each."""
+    for M in (si.PREFILL_M, 16):
+        for idx, (K, N) in enumerate(si.PREFILL_SHAPES):
+            t = host.int4_tensors(si.int4_linear(102 + idx, (0,), K, N))
+            x = host.bf16_tensor(si.bf16_normal(102 + idx, (9, M), (M, K)))
+            y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+            nbytes = w4.w4_gemm_workspace_bytes(M, K, N)
+            ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device="cuda") if nbytes else None
+            for _ in range(5):
+                w4.w4_gemm(x, t["qw"], t["s"], t["z"], y, workspace=ws)
+            torch.cuda.synchronize()
+            log(f"gemm calls: M={M} K={K} N={N} x5")
+    return 0
+
+
 def main() -> int:
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -450,6 +471,8 @@ def main() -> int:
 
     if args.counters:
         return counter_run(torch, host, si)
+    if args.gemm_calls:
+        return gemm_calls(w4, torch, host, si)
 
     log("generating and uploading the decode step (336 INT4 linears)")
     own = decode_linears(host, si, torch)
