@@ -27,7 +27,7 @@
 // workgroup's 64 rows are staged in LDS once, at the start.  At the end the
 // four k-slice waves' partial sums of each column block are added in a fixed
 // order through LDS.  Measured on MI355X, neither the matrix cores nor LDS
-// are saturated (about 20 % and 35 % busy); the waves mostly wait on the
+// are saturated (about 28 % and 55 % busy); the waves mostly wait on the
 // per-step chain of global load, LDS store, barrier and LDS read, which is
 // why four waves per SIMD run faster than one or two with larger tiles.
 //
