@@ -30,15 +30,21 @@
 //    stage t - 2; the staging waves split the stage's 64-chunk slots.  An
 //    input from outside the chain is loaded as soon as the buffer is free.
 //    An input that is an earlier GEMV's output is read from that GEMV's
-//    tagged copy (32-bit words bf16 | tag << 16, written by the producer with
+//    copy in the workspace (bf16, written by the producer with
 //    device-coherent stores): the staging waves poll it with device-coherent
-//    loads until every word carries the producer stage's tag of this launch,
+//    loads until none of its values is the empty mark (a NaN pattern),
 //    starting once their own workgroup has finished the producing stage.
 //
 // So a GEMV waits for exactly the outputs it reads, and nothing else
 // synchronises workgroups: there is no grid-wide barrier.  Each workgroup
-// counts its launches in its own workspace line; the count keeps the tags of
-// consecutive launches apart.  Every wait is bounded: past the spin limit
+// counts its launches in its own workspace line.  The copies come in two
+// halves: a launch writes and polls the half of its count's parity, and its
+// staging waves first mark the other half empty for the next launch (launches
+// of one chain run one after another, so nothing reads that half meanwhile).
+// A copy holds two bytes per value, half of what a value tagged with its
+// writer would take: every workgroup polls every input it stages, so the
+// polls' bytes are on the critical path of each boundary.
+// Every wait is bounded: past the spin limit
 // the waiter records an error in the workspace and goes on (a staging wave
 // stops staging), so the launch always ends.
 #include "chain.hpp"
@@ -78,15 +84,15 @@ struct Shared {
     unsigned abort;
     unsigned timed_out;  // a compute wave stopped waiting for its x (recorded at the end)
     unsigned base;       // launches this workgroup has run before this one
-    unsigned tag_base;  // (base * num_stages) mod 65535
+    uint32_t mirror_off;  // byte offset of this launch's half of the copies: (base & 1) * mirror_half_bytes
 };
 
-// Tag of the outputs stage t writes in this launch: never 0 (the value the
-// mirrors are cleared to), and different from the previous launch's tag for
-// the same stage as long as there are fewer than 65535 stages.
-__device__ __forceinline__ unsigned stage_tag(const Shared& sh, int t) { return (sh.tag_base + (unsigned)t) % 65535u + 1u; }
-
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Neither BF16 half of a polled word is the empty mark.
+__device__ __forceinline__ unsigned filled(uint32_t w) {
+    return (unsigned)((w & 0xFFFFu) != kChainMirrorEmpty) & (unsigned)((w >> 16) != kChainMirrorEmpty);
+}
 
 // s_waitcnt immediate that waits for vmcnt <= n only (expcnt and lgkmcnt at
 // their maxima): vmcnt bits 3:0 and 15:14.
@@ -222,7 +228,7 @@ __device__ __forceinline__ float slot(const TileRegs& R, int q, int i, int lane,
 // With a single segment every row of the tile uses the lane's same two x
 // chunks, read once per tile.
 __device__ __forceinline__ void compute(const ChainGemv& G, const Work& w, int lane, const TileRegs& R,
-                                        const unsigned char* xg, unsigned tag) {
+                                        const unsigned char* xg, uint32_t mirror_off, uint32_t mirror_half_bytes) {
     const int sp = G.sp, Cp = chain_x_chunks(G.C);
     const uint32_t bias = vgpr_const(kInt4BiasPair);
     float acc[kSlotRows];
@@ -252,9 +258,11 @@ __device__ __forceinline__ void compute(const ChainGemv& G, const Work& w, int l
         const uint16_t v = f32_to_bf16(total);
         const __amdgpu_buffer_rsrc_t ry = make_rsrc(G.y, (uint32_t)G.N * 2u);
         __builtin_amdgcn_raw_buffer_store_b16(v, ry, (int)((w.row + j) * 2), 0, 0);
-        if (G.ym) {  // the tagged copy a later GEMV polls for: one 32-bit device-coherent store
-            const __amdgpu_buffer_rsrc_t rm = make_rsrc(G.ym, (uint32_t)G.N * 4u);
-            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v | (tag << 16), rm, (int)((w.row + j) * 4), 0,
+        if (G.ym) {  // the copy a later GEMV polls for, in this launch's half: one device-coherent store
+            // The empty mark is a NaN; an output with exactly its bits is stored as another NaN.
+            const uint16_t m = v == kChainMirrorEmpty ? kChainMirrorNaN : v;
+            const __amdgpu_buffer_rsrc_t rm = make_rsrc(G.ym, mirror_half_bytes + (uint32_t)G.N * 2u);
+            __builtin_amdgcn_raw_buffer_store_b16(m, rm, (int)(mirror_off + (uint32_t)(w.row + j) * 2u), 0,
                                                   kAuxDeviceCoherent);
         }
     }
@@ -295,39 +303,28 @@ __device__ __forceinline__ void stage_load(const ChainLaunch& L, int g, int m, i
     for (int p = 0; p < 4; ++p) raw[p] = buf_load_b128<0>(rx, c * 64u + 16u * p, 0);
 }
 
-// x of chunk m * 64 + lane of GEMV g from its producer's tagged output:
-// poll (device-coherent loads, bounded) until all 32 words carry the
-// producer stage's tag, then keep the BF16 halves.  False on time-out.
+// x of chunk m * 64 + lane of GEMV g from its producer's copy in this
+// launch's half: poll (device-coherent loads, bounded) until none of its 32
+// values is the empty mark.  False on time-out.
 __device__ __forceinline__ bool stage_poll(const ChainLaunch& L, Shared& sh, int g, int m, int lane, u32x4_t raw[4]) {
     const ChainGemv& G = L.gemvs[g];
-    const __amdgpu_buffer_rsrc_t rm = make_rsrc(G.xm, (uint32_t)G.C * 128u);
-    const unsigned want = stage_tag(sh, G.xm_stage);
+    const uint32_t off = sh.mirror_off;
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(G.xm, off + (uint32_t)G.C * 64u);
     const int c = m * kWave + lane;
     bool done = c >= G.C;  // padding chunks are staged as zeros
-    u32x4_t w[8];
     unsigned n = 0;
     for (;;) {
         if (!done) {
 #pragma unroll
-            for (int p = 0; p < 8; ++p) w[p] = buf_load_b128_coherent(rm, (uint32_t)c * 128u + 16u * p, 0);
+            for (int p = 0; p < 4; ++p) raw[p] = buf_load_b128_coherent(rm, off + (uint32_t)c * 64u + 16u * p, 0);
             bool ok = true;
 #pragma unroll
-            for (int p = 0; p < 8; ++p)
-                ok &= ((w[p].x >> 16) == want) & ((w[p].y >> 16) == want) & ((w[p].z >> 16) == want) &
-                      ((w[p].w >> 16) == want);
+            for (int p = 0; p < 4; ++p) ok &= (filled(raw[p].x) & filled(raw[p].y) & filled(raw[p].z) & filled(raw[p].w)) != 0u;
             done = ok;
         }
         if (__builtin_amdgcn_ballot_w64(!done) == 0) break;
         if (lds_load(&sh.abort) || ++n > L.spin_limit) return false;
         __builtin_amdgcn_s_sleep(8);
-    }
-    // Word pairs (x_2i, x_2i+1) from the low halves of words 2i and 2i + 1.
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        raw[p].x = __builtin_amdgcn_perm(w[2 * p].y, w[2 * p].x, 0x05040100u);
-        raw[p].y = __builtin_amdgcn_perm(w[2 * p].w, w[2 * p].z, 0x05040100u);
-        raw[p].z = __builtin_amdgcn_perm(w[2 * p + 1].y, w[2 * p + 1].x, 0x05040100u);
-        raw[p].w = __builtin_amdgcn_perm(w[2 * p + 1].w, w[2 * p + 1].z, 0x05040100u);
     }
     return true;
 }
@@ -397,12 +394,24 @@ __device__ __forceinline__ bool lds_wait(const ChainLaunch& L, Shared& sh, F rea
 // stage t - 2; the staging waves split its 64-chunk slots.  An input from
 // outside the chain is loaded as soon as the buffer is free (while earlier
 // stages still run); an input that is an earlier GEMV's output is polled
-// from that GEMV's tagged copy until every word carries its writer's tag,
-// so a stage waits for exactly the outputs it reads and for nothing else.
+// from that GEMV's copy until none of its values is the empty mark, so a
+// stage waits for exactly the outputs it reads and for nothing else.
 // Polling starts once this workgroup has finished the latest stage the
 // inputs come from (x_after), so it overlaps any stage in between.
 // sh.staged[sid] counts the stages this wave has staged.
 __device__ void staging_wave(const ChainLaunch& L, Shared& sh, unsigned char* xl, int lane, int sid) {
+    // Mark the other half of the copies empty for the next launch, which
+    // writes and polls there (nothing in this launch reads it).  The halves
+    // are multiples of 128 bytes.
+    if (L.mirror_half_bytes) {
+        const uint32_t other = L.mirror_half_bytes - sh.mirror_off;  // the half this launch does not use
+        const __amdgpu_buffer_rsrc_t rm = make_rsrc(L.mirrors, 2u * L.mirror_half_bytes);
+        const uint32_t e = kChainMirrorEmpty | (kChainMirrorEmpty << 16);
+        const uint32_t n16 = L.mirror_half_bytes / 16u, step = (uint32_t)L.workers * kChainStagers * kWave;
+        for (uint32_t i = ((uint32_t)blockIdx.x * kChainStagers + sid) * kWave + lane; i < n16; i += step)
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{e, e, e, e}, rm,
+                                                   (int)(other + 16u * i), 0, kAuxDeviceCoherent);
+    }
     for (int t = 0; t < L.num_stages; ++t) {
         // Buffer free: every compute wave here is past stage t - 2.  A stage
         // that reads earlier outputs also waits until this workgroup's own
@@ -470,7 +479,7 @@ __device__ void compute_wave(const ChainLaunch& L, Shared& sh, const unsigned ch
     // is a dummy (an empty buffer range, which returns zeros without touching
     // memory), so every step issues the same loads and the compiler's wait
     // before a tile's math covers exactly that tile.  No wave ever waits for
-    // its own stores: readers poll the tagged outputs.
+    // its own stores: readers poll the output copies.
     TileRegs R0, R1;
     Work cur = a;
     Work nxt = advance(L, cur, v, W);
@@ -489,7 +498,8 @@ __device__ void compute_wave(const ChainLaunch& L, Shared& sh, const unsigned ch
             wait_x(cur.s);
             x_stage = cur.s;
         }
-        compute(Gc, cur, lane, Rc, xl + (size_t)(cur.s & 1) * kChainXLdsBytes + Gc.x_lds, stage_tag(sh, cur.s));
+        compute(Gc, cur, lane, Rc, xl + (size_t)(cur.s & 1) * kChainXLdsBytes + Gc.x_lds, sh.mirror_off,
+                L.mirror_half_bytes);
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("" ::: "memory");
         issue(G2, has_n2 ? n2 : cur, !has_n2, lane, Rc);
@@ -524,7 +534,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainStage* 
         sh.abort = 0;
         sh.timed_out = 0;
         sh.base = L.counters[(size_t)blockIdx.x * kChainLineWords];
-        sh.tag_base = (sh.base % 65535u) * ((unsigned)L.num_stages % 65535u) % 65535u;
+        sh.mirror_off = (sh.base & 1u) * L.mirror_half_bytes;
     }
     __syncthreads();
     if (wave >= 1 && wave <= kChainComputeWaves) {

@@ -1,6 +1,6 @@
 // Tables of the persistent decode-chain kernel, shared by the host planner
 // (w4_api.hip) and the kernel (chain.hip).  They live in the caller's
-// workspace, written once by w4_chain_create, beside the tagged copies of
+// workspace, written once by w4_chain_create, beside the copies of
 // the outputs that later GEMVs read.
 #pragma once
 
@@ -22,13 +22,14 @@ struct ChainGemv {
     int tile0;       // first tile of this GEMV in its stage (tiles are kChainTileRows / sp rows)
     int x_lds;       // byte offset of this GEMV's staged x in its LDS buffer
     int x_internal;  // 1: x is the output of an earlier GEMV of the chain (read from xm)
-    // Tagged outputs: word r = bf16 y[r] | tag << 16, the tag naming the
-    // launch and stage that wrote it.  ym: where this GEMV writes its own
-    // (null when no GEMV reads its output); xm: its producer's, read instead
-    // of x (null when x comes from outside the chain).
-    unsigned* ym;
-    const unsigned* xm;
-    int xm_stage;  // stage index of xm's writer (its tags)
+    // Copies of outputs that later GEMVs read, in the first half of the
+    // copies area (bf16 [N], padded to 64 values); a launch uses the half of
+    // its parity.  ym: where this GEMV writes its own (null when no GEMV reads
+    // its output); xm: its producer's, read instead of x (null when x comes
+    // from outside the chain).
+    uint16_t* ym;
+    const uint16_t* xm;
+    int xm_stage;  // stage index of xm's writer
     int x_slots;   // 64-chunk staging slots of x; 0 when an earlier GEMV of the stage has the same x
 };
 
@@ -59,7 +60,7 @@ __host__ __device__ inline int chain_x_chunks(int C) { return C <= 128 ? 128 : (
 __host__ __device__ inline int chain_x_lds_bytes(int C) { return 68 * chain_x_chunks(C); }
 
 // Workspace layout: [error line][per-workgroup launch counter lines][stages]
-// [gemvs][tagged outputs, mirror_words 32-bit words].
+// [gemvs][output copies: two halves of mirror_words bf16 values].
 struct ChainLayout {
     size_t err, counters, stages, gemvs, mirrors, total;
 };
@@ -74,7 +75,7 @@ inline ChainLayout chain_layout(int num_gemvs, int num_stages, size_t mirror_wor
     l.gemvs = (l.gemvs + 63) & ~(size_t)63;
     l.mirrors = l.gemvs + (size_t)num_gemvs * sizeof(ChainGemv);
     l.mirrors = (l.mirrors + 255) & ~(size_t)255;
-    l.total = l.mirrors + mirror_words * 4;
+    l.total = l.mirrors + mirror_words * 2 * 2;
     return l;
 }
 
@@ -86,7 +87,15 @@ struct ChainLaunch {
     int num_stages;
     int workers;  // workgroups, one per compute unit
     unsigned spin_limit;
+    uint16_t* mirrors;           // the output copies: two halves of mirror_half_bytes
+    uint32_t mirror_half_bytes;  // 2 * mirror_words (a multiple of 128)
 };
+
+// A value of an output copy that is not written yet: a NaN pattern.  The
+// halves are filled with it before use; a producer whose output has exactly
+// these bits stores kChainMirrorNaN instead.
+constexpr uint16_t kChainMirrorEmpty = 0xFFFFu;
+constexpr uint16_t kChainMirrorNaN = 0x7FC0u;
 
 hipError_t launch_chain(const ChainLaunch& l, hipStream_t stream);
 hipError_t chain_occupancy(int* blocks_per_cu);

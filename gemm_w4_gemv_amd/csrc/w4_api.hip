@@ -244,12 +244,12 @@ struct w4_chain {
 
 namespace {
 
-// Host analysis of a chain: validation, stages, producers and the tagged
+// Host analysis of a chain: validation, stages, producers and the
 // output copies (mirrors) the workspace must hold.
 struct ChainPlan {
     int num_stages = 0;
     std::vector<int> producer;      // GEMV whose output is this GEMV's x, or -1
-    std::vector<long> mirror_word;  // word offset of this GEMV's mirror, or -1 (no reader)
+    std::vector<long> mirror_word;  // offset in values of this GEMV's copy within each half, or -1 (no reader)
     size_t mirror_words = 0;
 };
 
@@ -315,6 +315,9 @@ w4_status plan_chain(const char* fn, const w4_gemv_desc* descs, int count, Chain
             plan.mirror_words += ((size_t)descs[j].N + 63) / 64 * 64;
         }
     }
+    if (plan.mirror_words > ((size_t)1 << 29))
+        return fail(W4_ERR_SHAPE, "%s: the outputs later GEMVs read total %zu values (limit 2^29)", fn,
+                    plan.mirror_words);
     return W4_OK;
 }
 
@@ -393,7 +396,7 @@ W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* wor
         st.ngemv += 1;
     }
     char* base = static_cast<char*>(workspace);
-    unsigned* mirrors = reinterpret_cast<unsigned*>(base + lay.mirrors);
+    uint16_t* mirrors = reinterpret_cast<uint16_t*>(base + lay.mirrors);
     for (int i = 0; i < count; ++i) {
         gemvs[i].ym = plan.mirror_word[i] >= 0 ? mirrors + plan.mirror_word[i] : nullptr;
         gemvs[i].xm = plan.producer[i] >= 0 ? mirrors + plan.mirror_word[plan.producer[i]] : nullptr;
@@ -417,9 +420,9 @@ W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* wor
     int workers = cus;  // one workgroup per compute unit, all resident at once
     if (workers > w4::kChainMaxWorkers) workers = w4::kChainMaxWorkers;
 
-    // Zero the counters and the mirrors (tag 0 is never a valid tag).
+    // Zero the counters; both halves of the output copies start empty.
     err = hipMemset(base, 0, lay.stages);
-    if (err == hipSuccess && plan.mirror_words) err = hipMemset(base + lay.mirrors, 0, plan.mirror_words * 4);
+    if (err == hipSuccess && plan.mirror_words) err = hipMemset(base + lay.mirrors, 0xFF, plan.mirror_words * 4);
     if (err == hipSuccess)
         err = hipMemcpy(base + lay.stages, stages.data(), stages.size() * sizeof(w4::ChainStage), hipMemcpyHostToDevice);
     if (err == hipSuccess)
@@ -435,6 +438,8 @@ W4_API w4_status w4_chain_create(const w4_gemv_desc* descs, int count, void* wor
     L.num_stages = num_stages;
     L.workers = workers;
     L.spin_limit = 1u << 20;
+    L.mirrors = mirrors;
+    L.mirror_half_bytes = (uint32_t)(plan.mirror_words * 2);
     *chain = new w4_chain{L};
     return W4_OK;
 }

@@ -222,9 +222,9 @@ W4_API void w4_graph_destroy(w4_graph_t graph);
  * the output y of a GEMV of an earlier stage, and then sees it complete.
  * Such an input must be exactly that output (same pointer, K equal to the
  * producer's N); a partial overlap is W4_ERR_UNSUPPORTED.  Inside the launch
- * a GEMV waits only for the output it reads (its readers poll a tagged copy
- * of it, kept in the workspace), so GEMVs that do not depend on each other
- * may overlap in time.  Hence an output may overwrite an earlier stage's
+ * a GEMV waits only for the output it reads (its readers poll a BF16 copy
+ * of it kept in the workspace, in one of two halves that alternate between
+ * runs), so GEMVs that do not depend on each other may overlap in time.  Hence an output may overwrite an earlier stage's
  * input only if its GEMV depends, through its chain of inputs, on that
  * earlier GEMV's output (W4_ERR_UNSUPPORTED otherwise).  An output must not
  * overlap any weight, scale or zero of the chain, any other output, or any
@@ -232,14 +232,16 @@ W4_API void w4_graph_destroy(w4_graph_t graph);
  * fit the kernel's LDS staging area: the sum over the stage's distinct
  * inputs (GEMVs with the same x share one copy) of 68 * P bytes, with
  * P = 128 for K <= 4096, 256 for K <= 8192 and 512 above, at most 65536
- * (W4_ERR_SHAPE from w4_chain_create otherwise).
+ * (W4_ERR_SHAPE from w4_chain_create otherwise).  The outputs that later
+ * GEMVs read may total at most 2^29 values (W4_ERR_SHAPE).
  * At most 65534 stages.
  *
  * w4_chain_workspace_bytes(descs, count) validates the descriptors and
  * returns the workspace size they need (0 if they are invalid; the reason
  * is in w4_last_error).  w4_chain_create validates the descriptors on the
- * host, then (blocking, not capturable) clears the workspace's counters and
- * tagged copies and writes the chain's tables into it; it never allocates
+ * host, then (blocking, not capturable) clears the workspace's counters,
+ * marks the output copies empty and writes the chain's tables into it; it
+ * never allocates
  * device memory.  The workspace (device memory, 256-byte aligned, at least
  * w4_chain_workspace_bytes(descs, count) bytes) belongs to the chain until
  * w4_chain_destroy.  w4_chain_run enqueues one run on ``stream`` (one kernel

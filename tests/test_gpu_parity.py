@@ -441,6 +441,49 @@ def test_chain_data_dependent():
     step.destroy()
 
 
+def test_chain_nan_outputs_and_alternating_copies():
+    """A producer whose outputs are NaN does not stall the GEMV that reads them,
+    and consecutive runs keep their output copies apart.
+
+    An input holding the all-ones BF16 pattern (a NaN, the same bits as the
+    copies' empty mark) makes every output of the first GEMV NaN; the second
+    GEMV reads them through the copy and must see them as written.  Runs use
+    the two halves of the copies in turn, and the inputs go finite, finite,
+    NaN, NaN, finite, finite, so every run finds in its half what the run two
+    before wrote, of the other kind, unless that half was marked empty again.
+    """
+    lin0 = si.int4_linear(9, (0,), 256, 128)
+    lin1 = si.int4_linear(9, (1,), 128, 64)
+    x_fin = si.bf16_normal(9, (2,), (256,))
+    x_nan = x_fin.copy()
+    x_nan[[3, 100]] = 0xFFFF
+    t0, t1 = host.int4_tensors(lin0), host.int4_tensors(lin1)
+    t0["x"] = host.bf16_tensor(x_fin)
+    t0["y"] = torch.zeros(128, dtype=torch.bfloat16, device=DEV)
+    t1["x"] = t0["y"]
+    t1["y"] = torch.zeros(64, dtype=torch.bfloat16, device=DEV)
+    t0["stage"], t1["stage"] = 0, 1
+    y0_ref, w0 = int4_ref(lin0, x_fin)
+    y1_ref, w1 = int4_ref(lin1, oracle.bf16_bits(y0_ref[0]))
+    step = DecodeStep([t0, t1], mode="chain")
+    for run, bad in enumerate([False, False, True, True, False, False]):
+        print(f"chain NaN/copies run {run} nan_input={bad}", flush=True)
+        t0["x"].copy_(host.bf16_tensor(x_nan if bad else x_fin))
+        t0["y"].zero_()
+        t1["y"].zero_()
+        torch.cuda.synchronize()
+        step.run_eager()
+        step.stream.synchronize()
+        assert step.chain.error() == 0, f"run {run}"
+        y0, y1 = host.bf16_values(t0["y"]), host.bf16_values(t1["y"])
+        if bad:
+            assert np.all(np.isnan(y0)) and np.all(np.isnan(y1)), f"run {run}"
+        else:
+            check_outputs(y0, y0_ref[0], xnorm(x_fin), w0, f"NaN/copies run {run} first GEMV")
+            check_outputs(y1, y1_ref[0], xnorm(oracle.bf16_bits(y0_ref[0])), w1, f"NaN/copies run {run} second GEMV")
+    step.destroy()
+
+
 @pytest.mark.parametrize("grouped", [False, True], ids=["six_stages_per_layer", "grouped_four_stages"])
 def test_chain_two_decoder_layers(grouped):
     """Two full decoder layers wired as a decoder reads them, as the timed decode step is
