@@ -324,7 +324,9 @@ __device__ __forceinline__ bool stage_poll(const ChainLaunch& L, Shared& sh, int
         }
         if (__builtin_amdgcn_ballot_w64(!done) == 0) break;
         if (lds_load(&sh.abort) || ++n > L.spin_limit) return false;
-        __builtin_amdgcn_s_sleep(8);
+        // A short pause: a round trip takes about a microsecond, and longer
+        // pauses (8) measured 2 % slower on the decode step.
+        __builtin_amdgcn_s_sleep(2);
     }
     return true;
 }
