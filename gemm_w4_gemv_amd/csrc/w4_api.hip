@@ -262,6 +262,8 @@ w4_status plan_chain(const char* fn, const w4_gemv_desc* descs, int count, Chain
         if (!d.x || !d.y) return fail(W4_ERR_NULL, "%s: descriptor %d: x and y must not be NULL", fn, i);
         w4_status st = check_int4(fn, d.qw, d.s, d.z, d.K, d.N, W4_INT4_GROUP, W4_CHAIN_MAX_K);
         if (st != W4_OK) return st;
+        if ((unsigned long long)d.N * (unsigned long long)(d.K / 2) > W4_GEMV_MAX_MATRIX_BYTES)
+            return fail(W4_ERR_SHAPE, "%s: descriptor %d: N * K / 2 exceeds %llu bytes", fn, i, W4_GEMV_MAX_MATRIX_BYTES);
         if (!aligned(d.x, 16) || !aligned(d.y, 2)) return fail(W4_ERR_ALIGN, "%s: descriptor %d: x or y misaligned", fn, i);
         if (d.reserved != 0) return fail(W4_ERR_ARG, "%s: descriptor %d: reserved must be 0", fn, i);
         if (d.stage < 0 || (i > 0 && d.stage < descs[i - 1].stage))

@@ -215,8 +215,9 @@ W4_API void w4_graph_destroy(w4_graph_t graph);
  * paragraph) names the remedy, a persistent kernel that fuses several GEMMs
  * into one launch.
  *
- * Each descriptor is one w4_gemv (same operands, layouts and limits, plus
- * K <= W4_CHAIN_MAX_K) tagged with a stage number.  Descriptors must be given
+ * Each descriptor is one w4_gemv (same operands, layouts and limits,
+ * N * K / 2 <= W4_GEMV_MAX_MATRIX_BYTES included, plus K <= W4_CHAIN_MAX_K)
+ * tagged with a stage number.  Descriptors must be given
  * in non-decreasing stage order.  The result is that of running the stages
  * one after another, each stage's GEMVs in any order: a GEMV may read as x
  * the output y of a GEMV of an earlier stage, and then sees it complete.

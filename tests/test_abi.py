@@ -207,12 +207,14 @@ def test_chain_validation():
     assert ws_bytes([]) == 0
     assert ws_bytes([desc(K=100)]) == 0                        # invalid descriptors
     # q (stage 0) -> o (stage 1) reading q's output exactly: the workspace
-    # also holds the tagged copy of q's 4096 outputs
+    # also holds two BF16 copies of q's 4096 outputs (one per run parity)
     q = desc(K=3840, N=4096, y=Y)
     o = desc(x=Y, K=4096, N=3840, y=Y + 65536, stage=1)
     assert ws_bytes([q, o]) >= ws_bytes([q, desc(N=3840, y=Y + 65536, stage=1)]) + 4096 * 4
     assert create([desc()], ws=None) == NULL
     assert create([desc(K=16384 + 128)]) == SHAPE          # the chain's K limit
+    assert create([desc(K=16384, N=1 << 20)]) == SHAPE     # N * K / 2 over the 32-bit offsets' range
+    assert ws_bytes([desc(K=16384, N=(1 << 19) - 1, qw=0x7E0000000000)]) > 0   # just under it (weights far from the rest)
     assert create([desc(K=100)]) == SHAPE
     assert create([desc(x=X + 8)]) == ALIGN
     assert create([desc()], ws=WSP + 128) == ALIGN           # workspace needs 256-byte alignment
