@@ -60,6 +60,7 @@ constexpr int kSZBytes = 2 * kBN * kMaxGroups * 2;  // s then z, [64][G] fp16 ea
 constexpr int kRedBytes = kWaves * kRB * kCBW * kWave * 16;
 constexpr int kLdsBytes = (kOffSZ + kSZBytes) > kRedBytes ? (kOffSZ + kSZBytes) : kRedBytes;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+static_assert(W4_GEMM_MAX_K <= W4_GEMV_MAX_K, "an M = 1 GEMM runs the GEMV kernel");
 
 __device__ __forceinline__ void mfma_16x16x32(const u32x4_t& a, const u32x4_t& b, f32x4_t& acc) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -303,6 +304,10 @@ size_t gemm_int4_workspace_bytes(int M, int K, int N) {
 
 hipError_t launch_gemm_int4(const void* x, const int32_t* qw, const void* s, const void* z,
                             void* y, int M, int K, int N, void* workspace, hipStream_t stream) {
+    // One row is a GEMV: its kernel streams the weights at a higher rate than
+    // the 16-row matrix-core block of the small-M path (K <= W4_GEMM_MAX_K ==
+    // W4_GEMV_MAX_K).
+    if (M == 1) return launch_gemv_int4(x, qw, s, z, y, K, N, stream);
     if (M <= kGemmSmallMMax) return launch_gemm_int4_small_m(x, qw, s, z, y, M, K, N, stream);
     const int splits = choose_splits(M, K, N);
     const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM), (unsigned)splits);

@@ -122,7 +122,8 @@ W4_API w4_status w4_gemv(const void* x, const int32_t* qw, const void* s, const 
  * dequantised BF16 weights into a tensor-core GEMM) and "INT4 融合 GEMV"
  * (equivalence tested at M = 128).  Here each packed word is dequantised in
  * registers straight into the matrix-core operand (BF16, round-to-nearest-
- * even) and the BF16 weight is never written to device memory.  M <= 16 (a
+ * even) and the BF16 weight is never written to device memory.  M = 1 runs
+ * w4_gemv's kernel (same result, bit for bit, as w4_gemv).  2 <= M <= 16 (a
  * few decode tokens at once) takes a streaming path instead: one 16-row
  * matrix-core block of x against the exact codes, the group's zero and scale
  * applied to the FP32 block sums, weights read once and no workspace.

@@ -268,6 +268,23 @@ def test_gemm_small_m(M, K, N):
     check_outputs(y[:, rows], y_ref, xnorm(x), wmax, f"gemm small M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("K,N", [(3840, 15360), (15360, 3840), (640, 1000), (32768, 64)])
+def test_gemm_single_row_is_the_gemv(K, N):
+    """w4_gemm at M = 1 gives exactly w4_gemv's output, and that matches the oracle."""
+    print(f"gemm M=1 K={K} N={N}", flush=True)
+    lin = si.int4_linear(26, (K, N), K, N)
+    x = si.bf16_normal(26, (K, N, 7), (1, K))
+    assert w4.w4_gemm_workspace_bytes(1, K, N) == 0
+    y, _ = run_gemm(lin, x)
+    t = host.int4_tensors(lin)
+    yv = torch.empty(N, dtype=torch.bfloat16, device=DEV)
+    w4.w4_gemv(host.bf16_tensor(x[0]), t["qw"], t["s"], t["z"], yv)
+    torch.cuda.synchronize()
+    assert np.array_equal(host.bf16_values(yv).view(np.uint64), y[0].view(np.uint64))  # bit for bit
+    y_ref, wmax = int4_ref(lin, x)
+    check_outputs(y, y_ref, xnorm(x), wmax, f"gemm M=1 K={K} N={N}")
+
+
 @pytest.mark.parametrize("M", [17, 32])
 def test_gemm_just_past_small_m(M):
     """M = 17 and 32 take the tiled GEMM (split K on this shape): every output."""
