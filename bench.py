@@ -288,14 +288,15 @@ def extra_workloads(w4, host, si, torch, rf):
         del copies
         log(f"prefill M=128 K={K} N={N}: {us:.1f} us, {tf:.0f} TFLOP/s")
 
-    # small-M decode (a few tokens at once) through w4_gemm's small-M path, on the
-    # gate/up and down shapes: weights are read once per call, so the rate is in GB/s
+    # small-M decode (a few tokens at once) through w4_gemm (M = 1: the GEMV kernel,
+    # M = 2: the two-row GEMV, M = 4 and 16: the matrix-core block), on the gate/up
+    # and down shapes: weights are read once per call, so the rate is in GB/s
     small = {}
     for si_idx, (K, N) in enumerate(si.PREFILL_SHAPES):
         per = rf.int4_weight_bytes(K, N)
         n_copies = -(-(512 * MB) // per) + 1
         copies = [host.int4_tensors(si.int4_linear(102 + si_idx, (c,), K, N)) for c in range(n_copies)]
-        for M in (1, 4, 16):
+        for M in (1, 2, 4, 16):
             x = host.bf16_tensor(si.bf16_normal(102 + si_idx, (10, M), (M, K)))
             y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
             g = capture(w4, torch, stream,

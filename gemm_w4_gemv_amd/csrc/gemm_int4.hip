@@ -308,6 +308,8 @@ hipError_t launch_gemm_int4(const void* x, const int32_t* qw, const void* s, con
     // the 16-row matrix-core block of the small-M path (K <= W4_GEMM_MAX_K ==
     // W4_GEMV_MAX_K).
     if (M == 1) return launch_gemv_int4(x, qw, s, z, y, K, N, stream);
+    // Two rows: still a GEMV, each unpacked word shared by both rows.
+    if (gemv_rows_int4_supports(M, K)) return launch_gemv_rows_int4(x, qw, s, z, y, M, K, N, stream);
     if (M <= kGemmSmallMMax) return launch_gemm_int4_small_m(x, qw, s, z, y, M, K, N, stream);
     const int splits = choose_splits(M, K, N);
     const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM), (unsigned)splits);

@@ -22,6 +22,11 @@ hipError_t launch_gemm_int4_small_m(const void* x, const int32_t* qw, const void
                                     void* y, int M, int K, int N, hipStream_t stream);
 hipError_t launch_gemm_int4(const void* x, const int32_t* qw, const void* s, const void* z,
                             void* y, int M, int K, int N, void* workspace, hipStream_t stream);
+// Two rows of x as a GEMV: each unpacked weight word is dotted with both
+// rows; K <= 16384 (x held in registers).
+bool gemv_rows_int4_supports(int M, int K);
+hipError_t launch_gemv_rows_int4(const void* x, const int32_t* qw, const void* s, const void* z, void* y,
+                                 int M, int K, int N, hipStream_t stream);
 
 hipError_t launch_moe_gemv_fp4(const void* x, int64_t x_stride, const uint8_t* qw,
                                const void* s, const int32_t* ids, void* y, int E,

@@ -123,8 +123,9 @@ W4_API w4_status w4_gemv(const void* x, const int32_t* qw, const void* s, const 
  * (equivalence tested at M = 128).  Here each packed word is dequantised in
  * registers straight into the matrix-core operand (BF16, round-to-nearest-
  * even) and the BF16 weight is never written to device memory.  M = 1 runs
- * w4_gemv's kernel (same result, bit for bit, as w4_gemv).  2 <= M <= 16 (a
- * few decode tokens at once) takes a streaming path instead: one 16-row
+ * w4_gemv's kernel (same result, bit for bit, as w4_gemv); M = 2 with
+ * K <= 16384 a GEMV over both rows (weights unpacked once, exact codes).
+ * Other M <= 16 (a few decode tokens at once) take a streaming path: one 16-row
  * matrix-core block of x against the exact codes, the group's zero and scale
  * applied to the FP32 block sums, weights read once and no workspace.
  *   x   device bf16 [M][K], 16-byte aligned   qw, s, z as for w4_gemv

@@ -254,9 +254,14 @@ def test_gemm_deterministic(M):
     (13, 640, 1000),     # 5 groups for 8 waves (some waves idle), ragged N
     (16, 256, 130),      # 2 groups
     (3, 4096, 262144),   # logits-sized N, 64-row tiles
+    (4, 15360, 3840),    # the down shape at M = 4
+    (2, 15360, 3840),    # two-row GEMV (M = 2, K <= 16384), four waves per row
+    (2, 640, 1000),      # two-row GEMV, one chunk per lane, ragged N
+    (2, 8192, 130),      # two-row GEMV, two waves per row
+    (2, 16512, 100),     # M = 2 with K past the two-row GEMV's limit: the matrix-core block
 ])
 def test_gemm_small_m(M, K, N):
-    """The small-M path of w4_gemm (M <= 16): sampled rows against the oracle."""
+    """The small-M paths of w4_gemm (2 <= M <= 16): sampled rows against the oracle."""
     print(f"gemm small M={M} K={K} N={N}", flush=True)
     lin = si.int4_linear(23, (M, K, N), K, N)
     x = si.bf16_normal(23, (M, K, N, 7), (M, K))
