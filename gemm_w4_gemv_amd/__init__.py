@@ -15,6 +15,7 @@ Tensor formats (see ``include/w4.h``):
 from __future__ import annotations
 
 import ctypes
+import os
 import pathlib
 
 import torch
@@ -28,7 +29,9 @@ __all__ = [
     "w4_chain_error", "w4_chain_destroy", "CHAIN_MAX_K", "w4_read_probe", "READ_PROBE_SINK",
 ]
 
-LIB_PATH = pathlib.Path(__file__).resolve().with_name("libw4.so")
+# W4_LIBRARY names another build of the same library (the chain-timeline build
+# of chain_timeline.py); by default the libw4.so next to this file.
+LIB_PATH = pathlib.Path(os.environ.get("W4_LIBRARY") or pathlib.Path(__file__).resolve().with_name("libw4.so"))
 INT4_GROUP = 128
 FP4_GROUP = 32
 GEMV_MAX_K = 32768

@@ -56,18 +56,21 @@ def _run(cmd):
     return res.returncode, "\n".join(lines)
 
 
-def build(verbose: bool = False, asm: bool = False, defines=()) -> pathlib.Path:
-    BUILD.mkdir(exist_ok=True)
+def build(verbose: bool = False, asm: bool = False, defines=(), lib: pathlib.Path = LIB,
+          build_dir: pathlib.Path = BUILD) -> pathlib.Path:
+    """Compile and link; ``defines`` (NAME or NAME=VALUE) go to every source."""
+    build_dir.mkdir(parents=True, exist_ok=True)
+    lib.parent.mkdir(parents=True, exist_ok=True)
     cc = hipcc()
     extra = [f"-D{d}" for d in defines]
     sources = sorted(CSRC.glob("*.hip"))
     jobs = []
     for src in sources:
-        obj = BUILD / (src.stem + ".o")
+        obj = build_dir / (src.stem + ".o")
         jobs.append(([cc, *flags(extra), "-c", str(src), "-o", str(obj)], obj))
         if asm:
             jobs.append(([cc, *flags(extra), "--cuda-device-only", "-S", str(src),
-                          "-o", str(BUILD / (src.stem + ".s"))], None))
+                          "-o", str(build_dir / (src.stem + ".s"))], None))
     workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(workers) as ex:
         results = list(ex.map(lambda j: (_run(j[0]), j[0]), jobs))
@@ -77,13 +80,13 @@ def build(verbose: bool = False, asm: bool = False, defines=()) -> pathlib.Path:
         if rc:
             raise RuntimeError(f"compile failed: {' '.join(cmd)}")
     objs = [str(o) for _, o in jobs if o is not None]
-    tmp = LIB.with_suffix(".so.tmp")
+    tmp = lib.with_suffix(".so.tmp")
     rc, out = _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *objs])
     if rc:
         print(out, file=sys.stderr)
         raise RuntimeError("link failed")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

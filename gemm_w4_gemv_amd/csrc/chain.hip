@@ -51,6 +51,19 @@
 #include "gemv_common.hpp"
 
 namespace w4 {
+
+#ifdef W4_CHAIN_TIMELINE
+// Timeline build only (chain_timeline.py): per workgroup and stage, four
+// s_memrealtime stamps (100 MHz) of the last launch: [0] its staging starts
+// (first staging wave), [1] its x is staged (last staging wave), [2] its
+// first tile's math starts (first compute wave), [3] its last tile's loads
+// for later stages are issued (last compute wave).  Workgroups and stages
+// past the bounds below are not recorded.
+constexpr int kTimelineStages = 512;
+constexpr int kTimelineWorkers = 256;
+__device__ unsigned g_chain_timeline[kTimelineWorkers * kTimelineStages * 4];
+#endif
+
 namespace {
 
 // Tile shape.  A tile is kSlotRows slot-rows x 2 chunks per lane.  A row of
@@ -85,7 +98,25 @@ struct Shared {
     unsigned timed_out;  // a compute wave stopped waiting for its x (recorded at the end)
     unsigned base;       // launches this workgroup has run before this one
     uint32_t mirror_off;  // byte offset of this launch's half of the copies: (base & 1) * mirror_half_bytes
+#ifdef W4_CHAIN_TIMELINE
+    unsigned timeline[kTimelineStages * 4];
+#endif
 };
+
+// Timeline stamp (timeline build only; called by one lane): the earliest or
+// the latest time event e of stage t was reached in this workgroup.
+__device__ __forceinline__ void timeline_mark(Shared& sh, int t, int e, bool earliest) {
+#ifdef W4_CHAIN_TIMELINE
+    if (t < kTimelineStages) {
+        const unsigned now = (unsigned)__builtin_amdgcn_s_memrealtime();
+        unsigned* p = &sh.timeline[t * 4 + e];
+        if (earliest) __hip_atomic_fetch_min(p, now, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        else __hip_atomic_fetch_max(p, now, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+#else
+    (void)sh, (void)t, (void)e, (void)earliest;
+#endif
+}
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -428,11 +459,13 @@ __device__ void staging_wave(const ChainLaunch& L, Shared& sh, unsigned char* xl
                                        lane < kChainComputeWaves &&
                                        lds_load(&sh.progress[lane < kChainComputeWaves ? lane : 0]) < need) == 0;
                         });
+        if (lane == 0) timeline_mark(sh, t, 0, true);
         if (!ok || !stage_share(L, sh, t, xl + (size_t)(t & 1) * kChainXLdsBytes, lane, sid)) {
             set_error(L, sh, 8u);
             return;
         }
         if (lane == 0) __hip_atomic_store(&sh.staged[sid], (unsigned)t + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (lane == 0) timeline_mark(sh, t, 1, false);
     }
 }
 
@@ -499,6 +532,7 @@ __device__ void compute_wave(const ChainLaunch& L, Shared& sh, const unsigned ch
         if (x_stage != cur.s) {
             wait_x(cur.s);
             x_stage = cur.s;
+            if (lane == 0) timeline_mark(sh, cur.s, 2, true);
         }
         compute(Gc, cur, lane, Rc, xl + (size_t)(cur.s & 1) * kChainXLdsBytes + Gc.x_lds, sh.mirror_off,
                 L.mirror_half_bytes);
@@ -506,6 +540,7 @@ __device__ void compute_wave(const ChainLaunch& L, Shared& sh, const unsigned ch
         asm volatile("" ::: "memory");
         issue(G2, has_n2 ? n2 : cur, !has_n2, lane, Rc);
         if (nxt.s != cur.s) report(nxt.s);  // cur was this wave's last tile of its stage
+        if (nxt.s != cur.s && lane == 0) timeline_mark(sh, cur.s, 3, false);
         if (!has_n) return false;
         cur = nxt;
         Gc = Gn;
@@ -538,6 +573,9 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainStage* 
         sh.base = L.counters[(size_t)blockIdx.x * kChainLineWords];
         sh.mirror_off = (sh.base & 1u) * L.mirror_half_bytes;
     }
+#ifdef W4_CHAIN_TIMELINE
+    for (int i = tid; i < kTimelineStages * 4; i += kChainThreads) sh.timeline[i] = (i & 1) ? 0u : ~0u;
+#endif
     __syncthreads();
     if (wave >= 1 && wave <= kChainComputeWaves) {
         const int W = L.workers * kChainComputeWaves;
@@ -556,6 +594,11 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainStage* 
     // Every wave has left its loop (all waits are bounded): count the launch.
     // The next launch of the chain reads the counter only after this one ends.
     __syncthreads();
+#ifdef W4_CHAIN_TIMELINE
+    if (blockIdx.x < kTimelineWorkers)
+        for (int i = tid; i < kTimelineStages * 4; i += kChainThreads)
+            g_chain_timeline[blockIdx.x * kTimelineStages * 4 + i] = sh.timeline[i];
+#endif
     if (tid == 0) {
         L.counters[(size_t)blockIdx.x * kChainLineWords] = sh.base + 1u;
         if (sh.timed_out) __hip_atomic_fetch_or(L.err, 16u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -574,3 +617,14 @@ hipError_t launch_chain(const ChainLaunch& l, hipStream_t stream) {
 }
 
 }  // namespace w4
+
+#ifdef W4_CHAIN_TIMELINE
+// Timeline build only: copy the stamps of the last launch (unsigned
+// [kTimelineWorkers][kTimelineStages][4], 100 MHz ticks) to host memory.
+// Synchronises the device first.  Returns a hipError_t value.
+extern "C" __attribute__((visibility("default"))) int w4_chain_timeline_read(void* host, size_t bytes) {
+    hipError_t err = hipDeviceSynchronize();
+    if (err == hipSuccess) err = hipMemcpyFromSymbol(host, HIP_SYMBOL(w4::g_chain_timeline), bytes);
+    return (int)err;
+}
+#endif

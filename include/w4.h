@@ -258,6 +258,9 @@ W4_API void w4_graph_destroy(w4_graph_t graph);
  * Errors: W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_UNSUPPORTED, W4_ERR_ALIGN,
  * W4_ERR_ALIAS, W4_ERR_ARG (no descriptors, stage order, too many stages),
  * W4_ERR_WORKSPACE, W4_ERR_HIP.
+ * (A separate build with -DW4_CHAIN_TIMELINE, made by
+ * gemm_w4_gemv_amd/chain_timeline.py for profiling, also exports
+ * w4_chain_timeline_read; the product library does not.)
  */
 #define W4_CHAIN_MAX_K 16384
 
