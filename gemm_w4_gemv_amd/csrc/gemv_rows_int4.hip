@@ -19,8 +19,10 @@
 //   * Measured on the decode shapes: M = 2 takes 11.3 / 11.8 us (K3840 ->
 //     N15360 / K15360 -> N3840) against 15.5 / 13.6 us on the 16-row
 //     matrix-core path.  Four rows (MX = 4, up to 198 VGPRs, two waves per
-//     SIMD) took 16.0 / 16.4 us, slower than that path (15.7 / 14.0), so
-//     M >= 3 stays there.
+//     SIMD) took 16.0 / 16.4 us, slower than that path (15.7 / 14.0), and
+//     fewer weight rows per wave to free registers was slower still (2 rows:
+//     21-23 us, 1 row: 30-33 us: fewer loads in flight), so M >= 3 stays
+//     there.
 #include "gemv_common.hpp"
 #include "w4_internal.hpp"
 
