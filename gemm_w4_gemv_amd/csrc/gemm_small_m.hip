@@ -251,7 +251,9 @@ hipError_t launch_gemm_int4_small_m(const void* x, const int32_t* qw, const void
     const uint16_t* zb = static_cast<const uint16_t*>(z);
     uint16_t* yb = static_cast<uint16_t*>(y);
     // The widest tile (64, 32 or 16 weight rows) that still gives at least
-    // 240 workgroups: wider tiles read the activations fewer times.
+    // 240 workgroups: wider tiles read the activations fewer times.  Asking
+    // for at least 480 or 960 workgroups instead was slower on K3840 ->
+    // N15360 (16.6-18.8 / 19.6-23.7 us at M = 4-16, against 15.9-16.8).
     auto launch = [&](auto cb) {
         constexpr int kCB = decltype(cb)::value;
         const dim3 grid((unsigned)((N + 16 * kCB - 1) / (16 * kCB)));
