@@ -112,34 +112,6 @@ def measured_traffic():
 
 
 # ------------------------------------------------------------------ helpers
-def decode_linears(host, si, torch):
-    """The 336 linears of the decode step, each reading its own seeded N(0,1) input."""
-    from gemm_w4_gemv_amd.decode import decoder_stages
-
-    lins = []
-    for layer, idx, name, K, N in si.decode_step_specs():
-        lin_np, x_bits = si.decode_linear(layer, idx)
-        t = host.int4_tensors(lin_np)
-        t["x"] = host.bf16_tensor(x_bits)
-        t["y"] = torch.zeros(N, dtype=torch.bfloat16, device="cuda")
-        t["name"], t["layer"], t["K"], t["N"] = name, layer, K, N
-        t["stage"] = decoder_stages([name], [layer])[0]
-        lins.append(t)
-    torch.cuda.synchronize()
-    return lins
-
-
-def linked_copy(lins):
-    """The same linears (same weights and output buffers), each reading the
-    output it reads in a decoder; layer 0's q, k and v read q's input."""
-    from gemm_w4_gemv_amd.decode import link_decoder_inputs
-    out = [dict(t) for t in lins]
-    for t in out[1:3]:
-        t["x"] = out[0]["x"]
-    link_decoder_inputs(out)
-    return out
-
-
 def time_graph(torch, replay, stream, reps: int, warmup: int = 2, trials: int = 5):
     """Milliseconds per replay: the median over ``trials`` of HIP events on ``stream`` around ``reps`` replays."""
     for _ in range(warmup):
@@ -408,8 +380,8 @@ def cpu_baseline(si, rf, layers: int):
 # --------------------------------------------------------------------- main
 def counter_run(torch, host, si) -> int:
     """Five chain launches of the decode step, then five 512 MiB torch copies."""
-    from gemm_w4_gemv_amd.decode import DecodeStep
-    lins = linked_copy(decode_linears(host, si, torch))
+    from gemm_w4_gemv_amd.decode import DecodeStep, decode_linears, linked_copy
+    lins = linked_copy(decode_linears())
     step = DecodeStep(lins, mode="chain")
     torch.cuda.synchronize()
     for _ in range(5):
@@ -468,7 +440,7 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
 
-    from gemm_w4_gemv_amd.decode import DecodeStep
+    from gemm_w4_gemv_amd.decode import DecodeStep, decode_linears, linked_copy
 
     if args.counters:
         return counter_run(torch, host, si)
@@ -476,7 +448,7 @@ def main() -> int:
         return gemm_calls(w4, torch, host, si)
 
     log("generating and uploading the decode step (336 INT4 linears)")
-    own = decode_linears(host, si, torch)
+    own = decode_linears()
     lins = linked_copy(own)
     n_stages = len({l["stage"] for l in lins})
     step_bytes = sum(rf.int4_linear_bytes(l["K"], l["N"]) for l in lins)

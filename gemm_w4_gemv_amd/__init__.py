@@ -24,7 +24,7 @@ __all__ = [
     "W4Error", "lib", "LIB_PATH", "w4_abi_version", "w4_status_string", "w4_last_error",
     "w4_gemv", "w4_gemm", "w4_gemm_workspace_bytes", "w4_moe_gemv", "w4_moe_gemm",
     "w4_graph_begin", "w4_graph_end", "w4_graph_replay", "w4_graph_destroy", "W4Graph",
-    "w4_dequant_int4", "w4_dequant_fp4", "INT4_GROUP", "FP4_GROUP", "GEMV_MAX_K",
+    "w4_dequant_int4", "w4_dequant_fp4", "w4_int4_gemv_operands", "INT4_GROUP", "FP4_GROUP", "GEMV_MAX_K",
     "GemvDesc", "W4Chain", "w4_chain_workspace_bytes", "w4_chain_create", "w4_chain_run",
     "w4_chain_error", "w4_chain_destroy", "CHAIN_MAX_K", "w4_read_probe", "READ_PROBE_SINK",
 ]
@@ -76,6 +76,7 @@ SIGNATURES = {
     "w4_chain_set_spin_limit": (_i32, [_vp, ctypes.c_uint32]),
     "w4_dequant_int4": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
     "w4_dequant_fp4": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _vp]),
+    "w4_int4_gemv_operands": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _vp]),
     "w4_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
 }
 
@@ -356,7 +357,7 @@ def w4_chain_destroy(chain: W4Chain) -> None:
 
 
 def w4_dequant_int4(qw, s, z, out_f32=None, out_bf16=None, group: int = INT4_GROUP, stream=None) -> None:
-    """Test-only: FP32 and/or BF16 image of an INT4 weight, from the GEMM's unpack code."""
+    """Test-only: FP32 values and/or BF16 matrix-core operand of an INT4 weight, from the prefill GEMM's routine."""
     N, K = qw.shape[0], qw.shape[1] * 8
     _, pq, ps, pz = _int4_weight(qw, s, z, K, group)
     pf = _dev(out_f32, "out_f32", (torch.float32,)) if out_f32 is not None else None
@@ -365,6 +366,25 @@ def w4_dequant_int4(qw, s, z, out_f32=None, out_bf16=None, group: int = INT4_GRO
         if t is not None and tuple(t.shape) != (N, K):
             raise ValueError(f"outputs must be [N, K] = {(N, K)}")
     _check(lib.w4_dequant_int4(pq, ps, pz, pf, pb, K, N, group, _stream(stream)), "w4_dequant_int4")
+
+
+def w4_int4_gemv_operands(qw, codes_out, x=None, x_out=None, stream=None) -> None:
+    """Test-only: the biased code pairs (int32 ``[N, K/8, 4]``) and, with ``x``, the matching x
+    pairs (int32 ``[K/8, 4]``) that the GEMV-path kernels dot, from their own routines."""
+    if not (isinstance(qw, torch.Tensor) and qw.dtype == torch.int32 and qw.dim() == 2):
+        raise ValueError("qw must be an int32 [N, K/8] tensor")
+    N, K = qw.shape[0], qw.shape[1] * 8
+    if tuple(codes_out.shape) != (N, K // 8, 4):
+        raise ValueError(f"codes_out must be [N, K/8, 4] = {(N, K // 8, 4)}")
+    if (x is None) != (x_out is None):
+        raise ValueError("x and x_out go together")
+    px = pxo = None
+    if x is not None:
+        if tuple(x.shape) != (K,) or tuple(x_out.shape) != (K // 8, 4):
+            raise ValueError("x must be [K] and x_out [K/8, 4]")
+        px, pxo = _dev(x, "x", _BF16), _dev(x_out, "x_out", (torch.int32,))
+    _check(lib.w4_int4_gemv_operands(_dev(qw, "qw", (torch.int32,)), px, _dev(codes_out, "codes_out", (torch.int32,)),
+                                     pxo, K, N, _stream(stream)), "w4_int4_gemv_operands")
 
 
 def w4_dequant_fp4(qw_fp4, s_fp4, out_f32=None, out_bf16=None, stream=None) -> None:

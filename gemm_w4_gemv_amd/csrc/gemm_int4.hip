@@ -81,24 +81,6 @@ struct Slot {
     uint32_t w;      // weight word (tid % 16) of row tid / 16
 };
 
-// bf16((q_e - z) * s) for the eight codes of one word, k order kept.
-// fma(q, s, -z s) is exact: q s and z s have at most 15 significant bits and
-// their difference (q - z) s is representable, so the one rounding is the
-// bf16 conversion (round to nearest even).
-__device__ __forceinline__ u32x4_t dequant_word_bf16(uint32_t w, float s, float nzs) {
-    uint32_t lo = w & 0x0F0F0F0Fu;         // codes of k = 8p + 0, 2, 4, 6
-    uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes of k = 8p + 1, 3, 5, 7
-    // Opaque to the optimiser, so each byte converts with one v_cvt_f32_ubyte{0..3}
-    // instead of a bit-field extract and a conversion.
-    asm volatile("" : "+v"(lo), "+v"(hi));
-    u32x4_t r;
-    r.x = pack_bf16x2(fmaf((float)(lo & 0xFFu), s, nzs), fmaf((float)(hi & 0xFFu), s, nzs));
-    r.y = pack_bf16x2(fmaf((float)((lo >> 8) & 0xFFu), s, nzs), fmaf((float)((hi >> 8) & 0xFFu), s, nzs));
-    r.z = pack_bf16x2(fmaf((float)((lo >> 16) & 0xFFu), s, nzs), fmaf((float)((hi >> 16) & 0xFFu), s, nzs));
-    r.w = pack_bf16x2(fmaf((float)(lo >> 24), s, nzs), fmaf((float)(hi >> 24), s, nzs));
-    return r;
-}
-
 template <bool kSplit>
 __global__ __launch_bounds__(kThreads) void gemm_int4_mfma_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ s,
@@ -222,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_mfma_kernel(
                 const int gi = g0 + min(j, nsteps - 1);
                 const float sc = f16_to_f32(lds_s[n * G + gi]);
                 const float zp = f16_to_f32(lds_z[n * G + gi]);
-                b[c] = dequant_word_bf16(q, sc, -zp * sc);
+                b[c] = int4_word_dequant_bf16(q, sc, -zp * sc);
             }
 #pragma unroll
             for (int r = 0; r < kRB; ++r) {

@@ -499,6 +499,26 @@ W4_API w4_status w4_dequant_int4(const int32_t* qw, const void* s, const void* z
     return err == hipSuccess ? W4_OK : hip_fail(err, fn);
 }
 
+W4_API w4_status w4_int4_gemv_operands(const int32_t* qw, const void* x, uint32_t* codes_out, uint32_t* x_out,
+                                       int K, int N, void* stream) {
+    const char* fn = "w4_int4_gemv_operands";
+    if (!qw || !codes_out) return fail(W4_ERR_NULL, "%s: qw and codes_out must not be NULL", fn);
+    if (!x != !x_out) return fail(W4_ERR_NULL, "%s: x and x_out must both be given or both be NULL", fn);
+    if (N < 0) return fail(W4_ERR_SHAPE, "%s: N = %d is negative", fn, N);
+    if (K <= 0 || K % 8 != 0) return fail(W4_ERR_SHAPE, "%s: K = %d is not a positive multiple of 8", fn, K);
+    if (!aligned(qw, 4) || !aligned(codes_out, 4) || (x && !aligned(x, 4)) || (x_out && !aligned(x_out, 4)))
+        return fail(W4_ERR_ALIGN, "%s: qw, x and the outputs must be 4-byte aligned", fn);
+    const Range ins[2] = {range(qw, (size_t)N * K / 2), range(x, x ? (size_t)K * 2 : 0)};
+    const Range outs[2] = {range(codes_out, (size_t)N * K * 2), range(x_out, x_out ? (size_t)K * 2 : 0)};
+    for (const Range& o : outs)
+        for (const Range& r : ins)
+            if (overlap(o, r)) return fail(W4_ERR_ALIAS, "%s: an output overlaps an input", fn);
+    if (overlap(outs[0], outs[1])) return fail(W4_ERR_ALIAS, "%s: the two outputs overlap", fn);
+    if (N == 0) return W4_OK;
+    hipError_t err = w4::launch_int4_gemv_operands(qw, x, codes_out, x_out, K, N, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4_OK : hip_fail(err, fn);
+}
+
 W4_API w4_status w4_dequant_fp4(const uint8_t* qw_fp4, const void* s_fp4, float* out_f32, void* out_bf16,
                                 int K, int N, void* stream) {
     const char* fn = "w4_dequant_fp4";

@@ -130,20 +130,38 @@ __device__ __forceinline__ void x_pairs_for_biased(const uint32_t xw[4], uint32_
     out[3] = (xw[1] >> 16) | (xw[3] & 0xFFFF0000u);
 }
 
-// Exact FP32 dequantisation of one word: out[j] = (q_j - z) * s.  (q - z) has
-// at most 5 significant bits and s 11, so the product is exact in FP32.
-__device__ __forceinline__ void int4_word_dequant_f32(uint32_t w, float s, float z, float out[8]) {
-    const uint32_t lo = w & 0x0F0F0F0Fu;         // codes of k = 8p + 0, 2, 4, 6 in bytes 0..3
-    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes of k = 8p + 1, 3, 5, 7
-    // (float)((v >> 8i) & 0xFF) is a single v_cvt_f32_ubyte{i}.
-    out[0] = ((float)(lo & 0xFFu) - z) * s;
-    out[1] = ((float)(hi & 0xFFu) - z) * s;
-    out[2] = ((float)((lo >> 8) & 0xFFu) - z) * s;
-    out[3] = ((float)((hi >> 8) & 0xFFu) - z) * s;
-    out[4] = ((float)((lo >> 16) & 0xFFu) - z) * s;
-    out[5] = ((float)((hi >> 16) & 0xFFu) - z) * s;
-    out[6] = ((float)(lo >> 24) - z) * s;
-    out[7] = ((float)(hi >> 24) - z) * s;
+// FP32 dequantisation of one word, as the prefill GEMM computes it:
+// out[j] = fma(q_j, s, nzs) with nzs = -z * s.  Exact: q s and z s have at
+// most 15 significant bits, and their difference (q - z) s is representable,
+// so the FMA's single rounding changes nothing.
+__device__ __forceinline__ void int4_word_dequant_f32(uint32_t w, float s, float nzs, float out[8]) {
+    uint32_t lo = w & 0x0F0F0F0Fu;         // codes of k = 8p + 0, 2, 4, 6 in bytes 0..3
+    uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes of k = 8p + 1, 3, 5, 7
+    // Opaque to the optimiser, so each byte converts with one v_cvt_f32_ubyte{0..3}
+    // instead of a bit-field extract and a conversion.
+    asm volatile("" : "+v"(lo), "+v"(hi));
+    out[0] = fmaf((float)(lo & 0xFFu), s, nzs);
+    out[1] = fmaf((float)(hi & 0xFFu), s, nzs);
+    out[2] = fmaf((float)((lo >> 8) & 0xFFu), s, nzs);
+    out[3] = fmaf((float)((hi >> 8) & 0xFFu), s, nzs);
+    out[4] = fmaf((float)((lo >> 16) & 0xFFu), s, nzs);
+    out[5] = fmaf((float)((hi >> 16) & 0xFFu), s, nzs);
+    out[6] = fmaf((float)(lo >> 24), s, nzs);
+    out[7] = fmaf((float)(hi >> 24), s, nzs);
+}
+
+// The prefill GEMM's matrix-core operand for one word: the eight dequantised
+// weights of int4_word_dequant_f32, in k order, each rounded once to BF16
+// (v_cvt_pk_bf16_f32, round to nearest even), two per 32-bit lane word.
+__device__ __forceinline__ u32x4_t int4_word_dequant_bf16(uint32_t w, float s, float nzs) {
+    float f[8];
+    int4_word_dequant_f32(w, s, nzs, f);
+    u32x4_t r;
+    r.x = pack_bf16x2(f[0], f[1]);
+    r.y = pack_bf16x2(f[2], f[3]);
+    r.z = pack_bf16x2(f[4], f[5]);
+    r.w = pack_bf16x2(f[6], f[7]);
+    return r;
 }
 
 // ------------------------------------------------------------------- FP4

@@ -38,6 +38,8 @@ hipError_t launch_moe_gemm_fp4(const void* x, const int32_t* row_start, const in
 
 hipError_t launch_dequant_int4(const int32_t* qw, const void* s, const void* z, float* out_f32,
                                void* out_bf16, int K, int N, hipStream_t stream);
+hipError_t launch_int4_gemv_operands(const int32_t* qw, const void* x, uint32_t* out_codes, uint32_t* out_x, int K,
+                                     int N, hipStream_t stream);
 hipError_t launch_dequant_fp4(const uint8_t* qw, const void* s, float* out_f32, void* out_bf16,
                               int K, int N, hipStream_t stream);
 

@@ -70,6 +70,41 @@ def link_decoder_inputs(linears) -> None:
         out[(layer, name)] = lin["y"]
 
 
+def decode_linears(device: str = "cuda"):
+    """The decode step's 336 INT4 linears as device tensors, from the seeded
+    synthetic workload (48 layers x q, k, v, o, gate, up, down; hidden 3840;
+    group 128), each reading its own seeded N(0,1) input and writing its own
+    zeroed output.  Each dict holds ``qw``, ``s``, ``z``, ``x``, ``y``,
+    ``name``, ``layer``, ``index`` (position in its layer), ``K``, ``N`` and
+    ``stage`` (six stages per layer).  The seeded inputs are synthetic data,
+    not part of the method: the generator module is imported here only."""
+    import seeded_inputs as si
+    from . import host
+
+    lins = []
+    for layer, idx, name, K, N in si.decode_step_specs():
+        lin_np, x_bits = si.decode_linear(layer, idx)
+        t = host.int4_tensors(lin_np, device)
+        t["x"] = host.bf16_tensor(x_bits, device)
+        t["y"] = torch.zeros(N, dtype=torch.bfloat16, device=device)
+        t["name"], t["layer"], t["index"], t["K"], t["N"] = name, layer, idx, K, N
+        t["stage"] = decoder_stages([name], [layer])[0]
+        lins.append(t)
+    torch.cuda.synchronize()
+    return lins
+
+
+def linked_copy(lins):
+    """The same linears (same weights and output buffers), each reading the
+    output it reads in a decoder (``link_decoder_inputs``); layer 0's q, k
+    and v share q's input.  This is the decode step as it is timed."""
+    out = [dict(t) for t in lins]
+    for t in out[1:3]:
+        t["x"] = out[0]["x"]
+    link_decoder_inputs(out)
+    return out
+
+
 class DecodeStep:
     """A captured chain of ``w4_gemv`` calls.
 

@@ -307,13 +307,20 @@ W4_API w4_status w4_chain_set_spin_limit(w4_chain_t chain, uint32_t spin_limit);
 W4_API w4_status w4_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 /*
- * Test-only dequantisers, sharing the device unpack code of the GEMM and the
- * FP4 GEMV.  They write the FP32 value of every weight (exact: at most 15
- * significant bits) and/or its BF16 round-to-nearest-even, so the packed
- * formats can be compared bit for bit with an independent reference.
- *   w4_dequant_int4: qw, s, z as for w4_gemv; out_f32 float [N][K];
- *                    out_bf16 bf16 [N][K]; either output may be NULL, not both.
- *   w4_dequant_fp4:  qw_fp4 uint8 [N][K/2], s_fp4 bf16 [N][K/32] (one expert).
+ * Test-only dequantisers.  They call the very device routines the hot
+ * kernels use to build their operands, so the packed formats can be compared
+ * bit for bit with an independent reference:
+ *   w4_dequant_int4: the prefill GEMM's dequantisation ("Lab 5", section
+ *                    "Python 反量化基线": the reference path materialises the
+ *                    BF16 weight (q - z) * s before F.linear).  out_f32 gets
+ *                    every weight's FP32 value as the GEMM computes it
+ *                    (exact: at most 15 significant bits), out_bf16 the
+ *                    GEMM's matrix-core operand, that value rounded to BF16
+ *                    (nearest even).  qw, s, z as for w4_gemv; out_f32 float
+ *                    [N][K]; out_bf16 bf16 [N][K]; either may be NULL, not both.
+ *   w4_dequant_fp4:  the FP4 kernels' unpack (E2M1 code pairs, even k low),
+ *                    times the BF16 scale in FP32, and its BF16 rounding.
+ *                    qw_fp4 uint8 [N][K/2], s_fp4 bf16 [N][K/32] (one expert).
  * Errors: as w4_gemv.
  */
 W4_API w4_status w4_dequant_int4(const int32_t* qw, const void* s, const void* z,
@@ -321,6 +328,25 @@ W4_API w4_status w4_dequant_int4(const int32_t* qw, const void* s, const void* z
                                  void* stream);
 W4_API w4_status w4_dequant_fp4(const uint8_t* qw_fp4, const void* s_fp4, float* out_f32,
                                 void* out_bf16, int K, int N, void* stream);
+
+/*
+ * Test-only: the operands of the GEMV-path kernels (w4_gemv, the decode
+ * chain, w4_gemm at M <= 16), from the same device routines.  Those kernels
+ * never scale the codes: they dot the biased codes 128 + q, exact in BF16,
+ * with x and apply zero and scale to the FP32 group sums,
+ * sum_k (q - z) s x = s (sum_k (128 + q) x - (128 + z) sum_k x)
+ * ("Lab 5", section "INT4 融合 GEMV": codes unpacked in registers, per-group
+ * scale and zero applied in the fused GEMV).
+ *   codes_out  uint32 [N][K/8][4]: for word p of row n, pair j (j = 0..3) is
+ *              the bf16 pair (128 + q[n][8p+j], 128 + q[n][8p+j+4]), low half first
+ *   x_out      uint32 [K/8][4]: pair j of word p is (x[8p+j], x[8p+j+4]), the
+ *              x pair each code pair is dotted with; x is bf16 [K]
+ *   qw, x and the outputs 4-byte aligned; K a positive multiple of 8;
+ *   x and x_out both given or both NULL.
+ * Errors: W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_ALIAS, W4_ERR_HIP.
+ */
+W4_API w4_status w4_int4_gemv_operands(const int32_t* qw, const void* x, uint32_t* codes_out,
+                                       uint32_t* x_out, int K, int N, void* stream);
 
 #ifdef __cplusplus
 }

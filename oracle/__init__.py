@@ -138,21 +138,13 @@ def linear(x, W) -> np.ndarray:
     return np.matmul(np.asarray(x, dtype=np.float64), np.asarray(W, dtype=np.float64).T)
 
 
-def gemm_int4(x_bits, qw, s_bits, z_bits, group: int = INT4_GROUP, rows=None) -> np.ndarray:
-    """FP64 ``y [M, N]`` for BF16 activations ``x_bits [M, K]`` and an INT4 linear.
-
-    ``rows`` (optional index array) restricts the computation to those output
-    rows n, for sampled checks of very large N.
-    """
+def gemm_int4(x_bits, qw, s_bits, z_bits, group: int = INT4_GROUP) -> np.ndarray:
+    """FP64 ``y [M, N]`` for BF16 activations ``x_bits [M, K]`` and an INT4 linear."""
     x = bf16_to_f64(np.atleast_2d(x_bits))
-    if rows is not None:
-        rows = np.asarray(rows)
-        qw, s_bits, z_bits = np.asarray(qw)[rows], np.asarray(s_bits)[rows], np.asarray(z_bits)[rows]
     return linear(x, dequant_int4(qw, s_bits, z_bits, group))
 
 
-def gemv_int4(x_bits, qw, s_bits, z_bits, group: int = INT4_GROUP, rows=None,
-              row_chunk: int = 8192) -> np.ndarray:
+def gemv_int4(x_bits, qw, s_bits, z_bits, group: int = INT4_GROUP, row_chunk: int = 8192) -> np.ndarray:
     """FP64 ``y [N]`` for one BF16 vector ``x_bits [K]`` (M = 1).
 
     Lab 5, "INT4 融合 GEMV": decode-time linears see a ``[1, hidden]`` input.
@@ -160,8 +152,6 @@ def gemv_int4(x_bits, qw, s_bits, z_bits, group: int = INT4_GROUP, rows=None,
     """
     x_bits = np.asarray(x_bits).reshape(1, -1)
     qw, s_bits, z_bits = np.asarray(qw), np.asarray(s_bits), np.asarray(z_bits)
-    if rows is not None:
-        return gemm_int4(x_bits, qw, s_bits, z_bits, group, rows=rows)[0]
     n = qw.shape[0]
     out = np.empty(n, dtype=np.float64)
     for r0 in range(0, n, row_chunk):
@@ -170,7 +160,7 @@ def gemv_int4(x_bits, qw, s_bits, z_bits, group: int = INT4_GROUP, rows=None,
     return out
 
 
-def moe_gemv_fp4(x_bits, pool_qw, pool_s, ids, rows=None) -> np.ndarray:
+def moe_gemv_fp4(x_bits, pool_qw, pool_s, ids) -> np.ndarray:
     """FP64 ``y [E, N]``: slot ``e`` applies expert ``ids[e]`` of the pool to ``x_e``.
 
     DeepSeek V4 Triton FP4, "深度分析" item 4: each token runs 2 FC per layer
@@ -185,10 +175,7 @@ def moe_gemv_fp4(x_bits, pool_qw, pool_s, ids, rows=None) -> np.ndarray:
         x_bits = np.broadcast_to(x_bits, (E, x_bits.shape[0]))
     ys = []
     for e in range(E):
-        qw_e, s_e = pool_qw[ids[e]], pool_s[ids[e]]
-        if rows is not None:
-            qw_e, s_e = qw_e[rows], s_e[rows]
-        W = dequant_fp4(qw_e, s_e)
+        W = dequant_fp4(pool_qw[ids[e]], pool_s[ids[e]])
         ys.append(linear(bf16_to_f64(x_bits[e])[None, :], W)[0])
     return np.stack(ys)
 

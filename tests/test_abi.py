@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     for name in names:
         assert hasattr(lib, name), f"libw4.so does not export {name}"
         assert name in w4.SIGNATURES, f"binding has no signature for {name}"
@@ -154,6 +154,16 @@ def test_graph_and_dequant_validation():
     assert lib.w4_dequant_int4(QW, S, Z, Y, None, 200, 4, 128, None) == SHAPE
     assert lib.w4_dequant_fp4(QW, S, None, None, 64, 4, None) == NULL
     assert lib.w4_dequant_fp4(QW, S, Y, None, 48, 4, None) == SHAPE
+    op = lib.w4_int4_gemv_operands
+    assert op(None, None, Y, None, 256, 4, None) == NULL
+    assert op(QW, X, Y, None, 256, 4, None) == NULL  # x without x_out
+    assert op(QW, None, Y, WSP, 256, 4, None) == NULL  # x_out without x
+    assert op(QW, None, Y, None, 12, 4, None) == SHAPE
+    assert op(QW, None, Y, None, 256, -1, None) == SHAPE
+    assert op(QW + 2, None, Y, None, 256, 4, None) == ALIGN
+    assert op(QW, X, QW + 64, WSP, 256, 4, None) == ALIAS  # codes_out over the weights
+    assert op(QW, X, Y, Y + 64, 256, 4, None) == ALIAS  # the two outputs overlap
+    assert op(QW, X, Y, WSP, 256, 0, None) == OK  # empty: nothing launched
 
 
 def test_chain_spin_limit_validation():

@@ -72,6 +72,27 @@ def test_dequant_int4_bit_exact(N, K):
     assert np.array_equal(host.bits_of(b16), oracle.bf16_bits(W))
 
 
+@pytest.mark.parametrize("N,K", [(37, 256), (5, 3840), (2, 15360), (1, 8)])
+def test_int4_gemv_operands_bit_exact(N, K):
+    """The operands of the GEMV, the chain, the two-row GEMV and the small-M
+    GEMM, from their own device routines: biased code pairs bf16(128 + q) in
+    the oracle's nibble order, and x pairs holding the same two k."""
+    lin = si.int4_linear(13, (N, K), K, N) if K % 128 == 0 else {
+        "qw": si.rng(13, N, K).integers(0, 2 ** 32, (N, K // 8), dtype=np.uint64).astype(np.uint32).view(np.int32)}
+    x_bits = si.bf16_normal(13, (1, N, K), (K,))
+    qw = torch.from_numpy(np.ascontiguousarray(lin["qw"]).view(np.int32)).to(DEV)
+    codes = torch.empty(N, K // 8, 4, dtype=torch.int32, device=DEV)
+    xo = torch.empty(K // 8, 4, dtype=torch.int32, device=DEV)
+    w4.w4_int4_gemv_operands(qw, codes, host.bf16_tensor(x_bits), xo)
+    torch.cuda.synchronize()
+    q = oracle.int4_codes(lin["qw"]).astype(np.float64).reshape(N, K // 8, 8)
+    lo = oracle.bf16_bits(128.0 + q[:, :, 0:4]).astype(np.uint32)
+    hi = oracle.bf16_bits(128.0 + q[:, :, 4:8]).astype(np.uint32)
+    assert np.array_equal(codes.cpu().numpy().view(np.uint32), lo | (hi << 16))
+    xb = np.asarray(x_bits, dtype=np.uint16).reshape(K // 8, 8).astype(np.uint32)
+    assert np.array_equal(xo.cpu().numpy().view(np.uint32), xb[:, 0:4] | (xb[:, 4:8] << 16))
+
+
 @pytest.mark.parametrize("N,K", [(33, 64), (128, 4096), (7, 2048), (2, 32)])
 def test_dequant_fp4_bit_exact(N, K):
     pool = si.fp4_pool(12, (N, K), 1, K, N)
@@ -156,22 +177,29 @@ def test_gemv_empty_is_noop():
 
 
 # ---------------------------------------------------------- decode-step graph
-def test_decode_step_graph_full_size():
-    """All 336 linears of the decode step, captured and replayed as the bench times them.
+@pytest.fixture(scope="module")
+def decode_step_data():
+    """The decode step's 336 linears (device tensors, each with its own seeded
+    input) built as the bench builds them, and their host bits for the oracle."""
+    from gemm_w4_gemv_amd.decode import decode_linears
+    lins = decode_linears()
+    host_in = [si.decode_linear(t["layer"], t["index"]) for t in lins]
+    yield lins, host_in
+    del lins, host_in
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_decode_step_graph_full_size(decode_step_data):
+    """All 336 linears of the decode step, captured and replayed as 336 launches.
 
     Graph replays equal the eager chain bit for bit (replays interleaved with
     other work), and every one of the 336 outputs matches the oracle on
     sampled rows.
     """
-    specs = si.decode_step_specs()
-    lins, host_in = [], []
-    for layer, idx, name, K, N in specs:
-        lin_np, x_bits = si.decode_linear(layer, idx)
-        t = host.int4_tensors(lin_np)
-        t["x"] = host.bf16_tensor(x_bits)
-        t["y"] = torch.zeros(N, dtype=torch.bfloat16, device=DEV)
-        lins.append(t)
-        host_in.append((lin_np, x_bits))
+    lins, host_in = decode_step_data
+    for t in lins:
+        t["y"].zero_()
     step = DecodeStep(lins)
     torch.cuda.synchronize()  # the zero fills above ran on the default stream
     step.run_eager()
@@ -191,11 +219,12 @@ def test_decode_step_graph_full_size():
     step.replay()
     step.stream.synchronize()
     g = si.rng(6, 0)
-    for (layer, idx, name, K, N), (lin_np, x_bits), t in zip(specs, host_in, lins):
+    for (lin_np, x_bits), t in zip(host_in, lins):
+        N = t["N"]
         rows = np.unique(np.concatenate([[0, N - 1], g.choice(N, 24, replace=False)]))
         y = host.bf16_values(t["y"])[rows]
         y_ref, wmax = int4_ref(lin_np, x_bits, rows)
-        check_outputs(y, y_ref[0], xnorm(x_bits), wmax, f"layer {layer} {name}")
+        check_outputs(y, y_ref[0], xnorm(x_bits), wmax, f"layer {t['layer']} {t['name']}")
     step.destroy()
 
 
@@ -380,23 +409,11 @@ def test_moe_small_shapes_and_determinism():
 
 
 # ------------------------------------------------------ persistent decode chain
-def _decode_linears(with_stage=True):
-    from gemm_w4_gemv_amd.decode import decoder_stages
-    lins, host_in, specs = [], [], si.decode_step_specs()
-    for layer, idx, name, K, N in specs:
-        lin_np, x_bits = si.decode_linear(layer, idx)
-        t = host.int4_tensors(lin_np)
-        t["x"] = host.bf16_tensor(x_bits)
-        t["y"] = torch.zeros(N, dtype=torch.bfloat16, device=DEV)
-        t["stage"] = decoder_stages([name], [layer])[0]
-        lins.append(t)
-        host_in.append((lin_np, x_bits))
-    return specs, lins, host_in
-
-
-def test_chain_decode_step_full_size():
-    """The 336-GEMV decode step as one persistent chain launch inside a graph (as the bench times it)."""
-    specs, lins, host_in = _decode_linears()
+def test_chain_decode_step_full_size(decode_step_data):
+    """The 336 GEMVs, each reading its own input, as one persistent chain launch inside a graph."""
+    lins, host_in = decode_step_data
+    for t in lins:
+        t["y"].zero_()
     step = DecodeStep(lins, mode="chain")
     torch.cuda.synchronize()
     step.run_eager()
@@ -414,12 +431,96 @@ def test_chain_decode_step_full_size():
             assert torch.equal(t["y"].view(torch.int16), e.view(torch.int16)), f"replay {rep} differs"
     assert step.chain.error() == 0
     g = si.rng(7, 0)
-    for (layer, idx, name, K, N), (lin_np, x_bits), t in zip(specs, host_in, lins):
+    for (lin_np, x_bits), t in zip(host_in, lins):
+        N = t["N"]
         rows = np.unique(np.concatenate([[0, N - 1], g.choice(N, 24, replace=False)]))
         y = host.bf16_values(t["y"])[rows]
         y_ref, wmax = int4_ref(lin_np, x_bits, rows)
-        check_outputs(y, y_ref[0], xnorm(x_bits), wmax, f"chain layer {layer} {name}")
+        check_outputs(y, y_ref[0], xnorm(x_bits), wmax, f"chain layer {t['layer']} {t['name']}")
     step.destroy()
+
+
+def same_bits_or_both_nan(a, b):
+    """Two bf16 tensors hold the same bits wherever either is not NaN (NaN payloads may differ)."""
+    both_nan = torch.isnan(a.float()) & torch.isnan(b.float())
+    return bool(torch.all((a.view(torch.int16) == b.view(torch.int16)) | both_nan))
+
+
+# Layers whose linked outputs are all finite: the values grow about 1000x per
+# layer (no norms or activations on this path) and layer 12's o overflows BF16.
+LINKED_FINITE_LAYERS = 12
+
+
+def test_chain_linked_decode_step_full_size(decode_step_data):
+    """The timed step itself: 336 GEMVs linked as a decoder reads them (o <- q,
+    gate/up <- o, down <- gate, next q/k/v <- down), 288 stages, one chain
+    launch replayed from a graph, exactly as bench.py builds it.
+
+    * error word 0, and three replays (outputs zeroed before each) identical bit for bit;
+    * every one of the 192 dependent boundaries delivered its producer's
+      complete output: the same GEMVs run without dependencies (grouped
+      schedule), each fed a copy of the input it read, give the same bits
+      for all 336 outputs (tile math depends only on the staged x);
+    * layers 0..11 (84 linears, every output finite) match the oracle on
+      every output, twice: against the oracle on the very input each GEMV
+      read, and against the oracle's own chain, run in order with each
+      intermediate rounded to BF16 as the chain stores it.
+    """
+    from gemm_w4_gemv_amd.decode import DECODER_INPUT, decoder_stages, linked_copy
+    own, host_in = decode_step_data
+    lins = linked_copy(own)
+    assert len({t["stage"] for t in lins}) == 288
+    assert sum(t["x"] is not own[0]["x"] for t in lins) == 333  # all but layer 0's q, k, v read an output
+    step = DecodeStep(lins, mode="chain")
+    step.capture()
+    outs = None
+    for rep in range(3):
+        for t in lins:
+            t["y"].zero_()
+        torch.cuda.synchronize()
+        step.replay()
+        step.stream.synchronize()
+        assert step.chain.error() == 0, f"replay {rep}: error word"
+        cur = [t["y"].clone() for t in lins]
+        if outs is None:
+            outs = cur
+        else:
+            for i, (a, b) in enumerate(zip(cur, outs)):
+                assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {rep} output {i} differs"
+    step.destroy()
+
+    # the same GEMVs with no dependencies, each reading a copy of what it read
+    clones = [dict(t, x=lt["x"].clone(), y=torch.zeros_like(t["y"]),
+                   stage=decoder_stages([t["name"]], [t["layer"]], grouped=True)[0]) for t, lt in zip(own, lins)]
+    ind = DecodeStep(clones, mode="chain")
+    torch.cuda.synchronize()
+    ind.run_eager()
+    ind.stream.synchronize()
+    assert ind.chain.error() == 0
+    for i, (c, o) in enumerate(zip(clones, outs)):
+        assert same_bits_or_both_nan(c["y"], o), f"linear {i} (layer {c['layer']} {c['name']}): linked output differs"
+    x_read = [host.bits_of(c["x"]) for c in clones[:7 * LINKED_FINITE_LAYERS]]
+    ind.destroy()
+    del clones
+
+    ref_out = {}
+    for i in range(7 * LINKED_FINITE_LAYERS):
+        t = own[i]
+        layer, name = t["layer"], t["name"]
+        lin_np = host_in[i][0]
+        src = DECODER_INPUT[name]
+        if src == "h":
+            x_ref = host_in[0][1] if layer == 0 else ref_out[(layer - 1, "down")]
+        else:
+            x_ref = ref_out[(layer, src)]
+        W = oracle.dequant_int4(lin_np["qw"], lin_np["s"], lin_np["z"])
+        y2 = oracle.linear(oracle.bf16_to_f64(np.stack([x_read[i], x_ref])), W)
+        wmax = np.abs(W).max(axis=1)
+        del W
+        y = host.bf16_values(outs[i])
+        check_outputs(y, y2[0], xnorm(x_read[i]), wmax, f"linked layer {layer} {name}, oracle on the input read")
+        check_outputs(y, y2[1], xnorm(x_ref), wmax, f"linked layer {layer} {name}, oracle chain")
+        ref_out[(layer, name)] = oracle.bf16_bits(y2[1])
 
 
 def test_chain_data_dependent():

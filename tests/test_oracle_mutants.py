@@ -70,8 +70,20 @@ def _round_half_up(v):
     return np.ldexp(np.floor(f * 256.0 + 0.5), e - 8)
 
 
-def _moe_ignores_ids(x_bits, pool_qw, pool_s, ids, rows=None):
-    return _orig["moe_gemv_fp4"](x_bits, pool_qw, pool_s, list(range(len(ids))), rows)
+def _moe_ignores_ids(x_bits, pool_qw, pool_s, ids):
+    return _orig["moe_gemv_fp4"](x_bits, pool_qw, pool_s, list(range(len(ids))))
+
+
+def _gemv_chunks_shifted(x_bits, qw, s_bits, z_bits, group=128, row_chunk=8192):
+    """Each row chunk after the first computed from the rows one place later (a slip in the chunk bounds)."""
+    y = _orig["gemv_int4"](x_bits, qw, s_bits, z_bits, group, row_chunk)
+    n = np.asarray(qw).shape[0]
+    if n > row_chunk:
+        shifted = _orig["gemv_int4"](x_bits, np.roll(qw, -1, axis=0), np.roll(s_bits, -1, axis=0),
+                                     np.roll(z_bits, -1, axis=0), group, row_chunk)
+        y = y.copy()
+        y[row_chunk:] = shifted[row_chunk:]
+    return y
 
 
 def _moe_gemm_group_shifted(x_bits, row_start, ids, pool_qw, pool_s, cols=None):
@@ -105,6 +117,7 @@ MUTANTS = {
     "fp4_group_of_16": ("dequant_fp4", _dequant_fp4_scale_by_k),
     "moe_gemm_group_boundary_off_by_one": ("moe_gemm_fp4", _moe_gemm_group_shifted),
     "moe_gemm_ids_ignored": ("moe_gemm_fp4", _moe_gemm_ids_ignored),
+    "gemv_row_chunks_shifted": ("gemv_int4", _gemv_chunks_shifted),
 }
 
 

@@ -175,6 +175,23 @@ def test_closed_form_int4():
         assert np.array_equal(y, np.full(N, K * (c - z0) * s0)), (c, z0, s0)
 
 
+@pytest.mark.parametrize("N,row_chunk", [(8192 + 37, 8192), (10, 3)])
+def test_gemv_row_chunks_closed_form(N, row_chunk):
+    """The GEMV oracle takes its rows in chunks (8192 by default): every row
+    past a chunk boundary still gives its own closed form.  Row n holds the
+    constant code c_n = n mod 16, zero z_n = (n / 16) mod 16 and scale
+    s_n = 2^-(1 + (n / 256) mod 8); with x = 1, y[n] = K (c_n - z_n) s_n."""
+    K = 128
+    n = np.arange(N)
+    c = n % 16
+    z = (n // 16) % 16
+    sv = 2.0 ** -(1 + (n // 256) % 8)
+    qw = np.repeat((c * 0x11111111).astype(np.uint32)[:, None], K // 8, axis=1).view(np.int32)
+    y = oracle.gemv_int4(bf16_bits_exact(np.ones(K, dtype=np.float32)), qw, f16_bits(sv[:, None]),
+                         f16_bits(z[:, None].astype(np.float64)), row_chunk=row_chunk)
+    assert np.array_equal(y, K * (c - z) * sv)
+
+
 def test_closed_form_fp4():
     """x = 1, every code c, scale s0: y = K * v(c) * s0 with v from the OCP table."""
     table = {int(k): v for k, v in load("fp4_e2m1.json")["table"].items()}
