@@ -35,6 +35,7 @@ LIB_PATH = pathlib.Path(os.environ.get("W4_LIBRARY") or pathlib.Path(__file__).r
 INT4_GROUP = 128
 FP4_GROUP = 32
 GEMV_MAX_K = 32768
+GEMM_NOALLOC_SCRATCH_BYTES = 16 << 20
 CHAIN_MAX_K = 16384
 
 STATUS = {0: "W4_OK", 1: "W4_ERR_NULL", 2: "W4_ERR_SHAPE", 3: "W4_ERR_UNSUPPORTED", 4: "W4_ERR_ALIGN",
@@ -62,6 +63,7 @@ SIGNATURES = {
     "w4_gemv": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
     "w4_gemm_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "w4_gemm": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "w4_gemm_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "w4_moe_gemv": (_i32, [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "w4_moe_gemm": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "w4_graph_begin": (_i32, [_vp]),

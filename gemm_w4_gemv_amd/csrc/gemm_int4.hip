@@ -34,6 +34,8 @@
 // When the tiles cannot fill the GPU, K is split across workgroups; each
 // split writes FP32 partials to the caller's workspace and a second kernel
 // adds them in split order (deterministic, no atomics).
+#include <mutex>
+
 #include "w4.h"
 #include "w4_device.hpp"
 #include "w4_internal.hpp"
@@ -312,6 +314,34 @@ hipError_t launch_gemm_int4(const void* x, const int32_t* qw, const void* s, con
     const unsigned blocks = (unsigned)((count + 255) / 256);
     splitk_reduce_kernel<<<blocks, 256, 0, stream>>>(ws, yb, count, splits);
     return hipGetLastError();
+}
+
+// Scratch for w4_gemm_noalloc, the entry point for callers that cannot
+// allocate: the split-K partial sums go here instead of into a workspace of
+// the caller's.  A __device__ array: every GPU the library runs on holds its
+// own copy until the process ends, and every call on that GPU shares it.  In
+// host code the array's name is not a device address; its address on the
+// current device comes from hipGetSymbolAddress, resolved once per device on
+// that device's first call and kept.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t gemm_noalloc_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* per_device[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!per_device[dev]) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        per_device[dev] = p;
+    }
+    *ptr = per_device[dev];
+    return hipSuccess;
 }
 
 }  // namespace w4

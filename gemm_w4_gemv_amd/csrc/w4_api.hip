@@ -134,6 +134,38 @@ W4_API w4_status w4_gemm(const void* x, const int32_t* qw, const void* s, const 
     return err == hipSuccess ? W4_OK : hip_fail(err, fn);
 }
 
+W4_API w4_status w4_gemm_noalloc(const void* x, const int32_t* qw, const void* s, const void* z, void* y, int M,
+                                 int K, int N, int g, void* stream) {
+    const char* fn = "w4_gemm_noalloc";
+    if (!x || !y) return fail(W4_ERR_NULL, "%s: x and y must not be NULL", fn);
+    w4_status st = check_int4(fn, qw, s, z, K, N, g, W4_GEMM_MAX_K);
+    if (st != W4_OK) return st;
+    if (M < 0) return fail(W4_ERR_SHAPE, "%s: M = %d is negative", fn, M);
+    if ((unsigned long long)M * (unsigned long long)K * 2ull > W4_GEMV_MAX_MATRIX_BYTES ||
+        (unsigned long long)N * (unsigned long long)(K / 2) > W4_GEMV_MAX_MATRIX_BYTES)
+        return fail(W4_ERR_SHAPE, "%s: M * K * 2 or N * K / 2 exceeds %llu bytes", fn, W4_GEMV_MAX_MATRIX_BYTES);
+    if (!aligned(x, 16)) return fail(W4_ERR_ALIGN, "%s: x must be 16-byte aligned", fn);
+    if (!aligned(y, 2)) return fail(W4_ERR_ALIGN, "%s: y must be 2-byte aligned", fn);
+    const size_t need = w4_gemm_workspace_bytes(M, K, N, g);
+    if (need > W4_GEMM_NOALLOC_SCRATCH_BYTES)
+        return fail(W4_ERR_WORKSPACE, "%s: M = %d, K = %d, N = %d needs %zu bytes of split-K scratch, above the "
+                    "library's %llu", fn, M, K, N, need, (unsigned long long)W4_GEMM_NOALLOC_SCRATCH_BYTES);
+    const Range ry = range(y, (size_t)M * N * 2);
+    const size_t sz_bytes = (size_t)N * (K / g) * 2;
+    const Range ins[4] = {range(x, (size_t)M * K * 2), range(qw, (size_t)N * K / 2), range(s, sz_bytes),
+                          range(z, sz_bytes)};
+    for (const Range& r : ins)
+        if (overlap(ry, r)) return fail(W4_ERR_ALIAS, "%s: y overlaps an input", fn);
+    if (M == 0 || N == 0) return W4_OK;
+    void* scratch = nullptr;
+    if (need > 0) {
+        hipError_t err = w4::gemm_noalloc_scratch(&scratch);
+        if (err != hipSuccess) return hip_fail(err, fn);
+    }
+    hipError_t err = w4::launch_gemm_int4(x, qw, s, z, y, M, K, N, scratch, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4_OK : hip_fail(err, fn);
+}
+
 W4_API w4_status w4_moe_gemv(const void* x, int64_t x_stride, const uint8_t* qw_fp4, const void* s_fp4,
                              const int32_t* expert_ids, void* y, int E, int num_experts, int K, int N,
                              void* stream) {

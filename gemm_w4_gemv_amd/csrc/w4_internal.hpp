@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "w4.h"
+
 namespace w4 {
 
 hipError_t launch_gemv_int4(const void* x, const int32_t* qw, const void* s, const void* z,
@@ -22,6 +24,10 @@ hipError_t launch_gemm_int4_small_m(const void* x, const int32_t* qw, const void
                                     void* y, int M, int K, int N, hipStream_t stream);
 hipError_t launch_gemm_int4(const void* x, const int32_t* qw, const void* s, const void* z,
                             void* y, int M, int K, int N, void* workspace, hipStream_t stream);
+// The split-K scratch of w4_gemm_noalloc: its size, and its address on the
+// current device (resolved on the device's first call, then kept).
+constexpr size_t kNoAllocScratchBytes = W4_GEMM_NOALLOC_SCRATCH_BYTES;
+hipError_t gemm_noalloc_scratch(void** ptr);
 // Two rows of x as a GEMV: each unpacked weight word is dotted with both
 // rows; K <= 16384 (x held in registers).
 bool gemv_rows_int4_supports(int M, int K);

@@ -146,6 +146,24 @@ W4_API w4_status w4_gemm(const void* x, const int32_t* qw, const void* s, const 
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * w4_gemm_noalloc -- w4_gemm for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): same operation, kernels, limits and result, bit for bit, but no
+ * workspace argument.  The split-K partial sums go to a scratch array the
+ * library holds on each GPU it runs on (W4_GEMM_NOALLOC_SCRATCH_BYTES, kept
+ * until the process ends); the call itself allocates nothing.  Shapes whose
+ * w4_gemm_workspace_bytes() exceeds that size are rejected (W4_ERR_WORKSPACE).
+ * Every call on a GPU shares its scratch: calls that may overlap in time on
+ * one GPU (different streams, or several threads) race and must be ordered
+ * by the caller.  The scratch holds only values each call writes before it
+ * reads them.  The first call on a device looks up the scratch's address.
+ * Errors: as w4_gemm.
+ */
+#define W4_GEMM_NOALLOC_SCRATCH_BYTES (16ull << 20)
+W4_API w4_status w4_gemm_noalloc(const void* x, const int32_t* qw, const void* s, const void* z,
+                                 void* y, int M, int K, int N, int g, void* stream);
+
+/*
  * w4_moe_gemv -- FP4 expert GEMVs, M = 1 per slot.
  *   y[e][n] = bf16( sum_k e2m1(c[ids[e]][n][k]) * s[ids[e]][n][k/32] * x_e[k] ),  e < E
  *   with x_e = x + e * x_stride (elements); x_stride = 0 shares one vector.

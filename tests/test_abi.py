@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     for name in names:
         assert hasattr(lib, name), f"libw4.so does not export {name}"
         assert name in w4.SIGNATURES, f"binding has no signature for {name}"
@@ -164,6 +164,18 @@ def test_graph_and_dequant_validation():
     assert op(QW, X, QW + 64, WSP, 256, 4, None) == ALIAS  # codes_out over the weights
     assert op(QW, X, Y, Y + 64, 256, 4, None) == ALIAS  # the two outputs overlap
     assert op(QW, X, Y, WSP, 256, 0, None) == OK  # empty: nothing launched
+
+
+def test_gemm_noalloc_validation():
+    na = lib.w4_gemm_noalloc
+    assert na(None, QW, S, Z, Y, 128, 3840, 64, 128, None) == NULL
+    assert na(X, QW, S, Z, Y, 128, 200, 64, 128, None) == SHAPE
+    assert na(X, QW, S, Z, Y, -1, 256, 64, 128, None) == SHAPE
+    assert na(X, QW, S, Z, Y, 128, 256, 64, 64, None) == UNSUP
+    assert na(X + 8, QW, S, Z, Y, 128, 256, 64, 128, None) == ALIGN
+    assert na(X, QW, S, Z, X + 64, 128, 256, 64, 128, None) == ALIAS
+    assert na(X, QW, S, Z, Y, 0, 256, 64, 128, None) == OK  # empty: nothing launched, no scratch looked up
+    assert f"W4_GEMM_NOALLOC_SCRATCH_BYTES ({w4.GEMM_NOALLOC_SCRATCH_BYTES >> 20}ull << 20)" in HEADER.read_text()
 
 
 def test_chain_spin_limit_validation():
