@@ -77,7 +77,12 @@ constexpr int kSlotLanes = kWave / kSlotRows;  // lanes per slot-row after the r
 
 struct TileRegs {
     u32x4_t w[2 * kSlotRows];  // slot (q, i) in w[2 q + i]
-    uint16_t sz[kSlotRows];    // lane l < 32: scale of group l of the slot-row's segment; l >= 32: zero of l - 32
+    // Per slot-row, one 16-bit value per lane: lane l < 32 holds the scale of
+    // group l of the slot-row's segment, lane l >= 32 the zero of group l - 32.
+    // Each lane's own pair is gathered from these at use (one VGPR per
+    // slot-row; loading each lane's four values would take three more, past
+    // the register budget of four waves per SIMD).
+    uint16_t sz[kSlotRows];
 };
 
 // A compute wave's position: tile t of stage s, i.e. rows [row, row + nrows)
@@ -244,7 +249,9 @@ __device__ __forceinline__ float lds_x_chunk(const unsigned char* xg, int Cp, in
     return *reinterpret_cast<const float*>(xg + (size_t)64 * Cp + (size_t)c * 4);
 }
 
-// One slot: chunk (q, i) of the tile, scale/zero shuffled from the slot-row's load.
+// One slot: chunk (q, i) of the tile.  Its group within the segment is
+// (l + 64 i) / 4; scale and zero come from the lanes that loaded them (a
+// gather, lane l reading lane l / 4 + 16 i, through ds_bpermute).
 __device__ __forceinline__ float slot(const TileRegs& R, int q, int i, int lane, const uint32_t xp[16], float sx,
                                       uint32_t bias, float acc) {
     const int gs = (lane + kWave * i) >> 2;  // group within the segment, 0..31
@@ -282,8 +289,11 @@ __device__ __forceinline__ void compute(const ChainGemv& G, const Work& w, int l
         }
     }
     float total = reduce_rows<kSlotRows>(acc, lane);  // lane L: slot-row L / kSlotLanes
-    if (sp >= 2) total += __shfl_xor(total, kSlotLanes, kWave);
-    if (sp == 4) total += __shfl_xor(total, 2 * kSlotLanes, kWave);
+    // A row's segments sit on consecutive slot-rows: lanes kSlotLanes (and
+    // 2 kSlotLanes) apart.
+    static_assert(kSlotLanes == 16, "segment sums cross lane bits 4 and 5");
+    if (sp >= 2) total = pair_sum<16>(total);
+    if (sp == 4) total = pair_sum<32>(total);
     const int j = (lane / kSlotLanes) >> seg_shift(sp);  // row of the tile this lane's total belongs to
     if ((lane & (kSlotLanes * sp - 1)) == 0 && j < w.nrows) {
         const uint16_t v = f32_to_bf16(total);

@@ -182,10 +182,63 @@ __device__ __forceinline__ void fp4_word_pairs(uint32_t w, uint32_t out[4]) {
 }
 
 // -------------------------------------------------------------- reductions
+// Cross-lane exchanges without LDS: DPP inside a row of 16 lanes, the gfx950
+// row swaps (v_permlane16_swap, v_permlane32_swap) across rows.
+
+// Value of lane l ^ m for an exchange across bit kOff (kOff = 1, 2, 4, 8) of
+// a 16-lane row: quad_perm [1,0,3,2] (m = 1), quad_perm [2,3,0,1] (m = 2),
+// row_half_mirror (m = 7) and row_ror:8 (m = 8).  Each partner differs from l
+// in bit kOff and above it in nothing, which is all a butterfly over bits
+// kOff, kOff / 2, ..., 1 needs: the masks stay independent, so every lane of
+// the row is summed exactly once.
+template <int kOff>
+__device__ __forceinline__ float dpp_partner(float v) {
+    constexpr int kCtrl = kOff == 1 ? 0xB1 : kOff == 2 ? 0x4E : kOff == 4 ? 0x141 : 0x128;
+    static_assert(kOff == 1 || kOff == 2 || kOff == 4 || kOff == 8, "DPP exchanges stay inside a row of 16");
+    const int b = __builtin_bit_cast(int, v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, kCtrl, 0xF, 0xF, false));
+}
+
+// For an exchange across lane bit kOff = 16 or 32: with a the value of lanes
+// whose bit is clear and b of lanes whose bit is set, returns a's sum over
+// the lane pair in the lanes with the bit clear and b's in the others.  The
+// swap instruction exchanges b's clear-bit rows with a's set-bit rows, so
+// adding its two outputs gives each lane its own pair sum.
+template <int kOff>
+__device__ __forceinline__ float swap_pair_sum(float a, float b) {
+    static_assert(kOff == 16 || kOff == 32, "row swaps cross bit 4 or 5");
+    const uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
+    uint32_t r0, r1;
+    if constexpr (kOff == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(ua, ub, false, false);
+        r0 = r[0];
+        r1 = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane16_swap(ua, ub, false, false);
+        r0 = r[0];
+        r1 = r[1];
+    }
+    // Scalars first: a bit_cast applied directly to the vector element r[1]
+    // reads element 0 with this compiler.
+    return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+
+// Sum of v over the lane pair across bit kOff, in every lane.
+template <int kOff>
+__device__ __forceinline__ float pair_sum(float v) {
+    if constexpr (kOff >= 16) {
+        return swap_pair_sum<kOff>(v, v);
+    } else {
+        return v + dpp_partner<kOff>(v);
+    }
+}
+
 // Reduce R per-lane values (one per row) across the 64 lanes of a wave.
-// Each step halves the rows a lane carries by exchanging the other half with
-// the partner lane, so R rows cost R - 1 + log2(64 / R) exchanges instead of
-// 6 R.  On return every lane holds the total of row lane / (64 / R).
+// Each step halves the rows a lane carries: across lane bit kOff, lanes with
+// the bit clear keep rows [0, R/2) and the others rows [R/2, R), each adding
+// its partner's value of the rows it keeps.  R rows cost R - 1 + log2(64 / R)
+// exchanges instead of 6 R.  On return every lane holds the total of row
+// lane / (64 / R).  The summation order is fixed, so results are reproducible.
 template <int R, int kOff>
 struct RowReduce {
     static __device__ __forceinline__ void run(float* v, int lane) {
@@ -194,13 +247,16 @@ struct RowReduce {
             const bool upper = (lane & kOff) != 0;
 #pragma unroll
             for (int i = 0; i < H; ++i) {
-                const float send = upper ? v[i] : v[i + H];
-                const float keep = upper ? v[i + H] : v[i];
-                v[i] = keep + __shfl_xor(send, kOff, kWave);
+                if constexpr (kOff >= 16) {
+                    v[i] = swap_pair_sum<kOff>(v[i], v[i + H]);
+                } else {
+                    const float lo = pair_sum<kOff>(v[i]), hi = pair_sum<kOff>(v[i + H]);
+                    v[i] = upper ? hi : lo;
+                }
             }
             RowReduce<H, kOff / 2>::run(v, lane);
         } else if constexpr (kOff >= 1) {
-            v[0] += __shfl_xor(v[0], kOff, kWave);
+            v[0] = pair_sum<kOff>(v[0]);
             RowReduce<1, kOff / 2>::run(v, lane);
         }
     }
