@@ -27,6 +27,7 @@ __all__ = [
     "w4_dequant_int4", "w4_dequant_fp4", "w4_int4_gemv_operands", "INT4_GROUP", "FP4_GROUP", "GEMV_MAX_K",
     "GemvDesc", "W4Chain", "w4_chain_workspace_bytes", "w4_chain_create", "w4_chain_run",
     "w4_chain_error", "w4_chain_destroy", "CHAIN_MAX_K", "w4_read_probe", "READ_PROBE_SINK",
+    "w4_tune_param", "w4_tune_force", "TUNE_KERNELS", "w4_gemm_noalloc",
 ]
 
 # W4_LIBRARY names another build of the same library (the chain-timeline build
@@ -36,6 +37,8 @@ INT4_GROUP = 128
 FP4_GROUP = 32
 GEMV_MAX_K = 32768
 GEMM_NOALLOC_SCRATCH_BYTES = 16 << 20
+# launch-tuning kernel families (W4_TUNE_*), name -> id
+TUNE_KERNELS = {"gemv": 0, "gemv_rows2": 1, "gemm_small_m": 2, "gemm": 3, "moe_gemv": 4}
 CHAIN_MAX_K = 16384
 
 STATUS = {0: "W4_OK", 1: "W4_ERR_NULL", 2: "W4_ERR_SHAPE", 3: "W4_ERR_UNSUPPORTED", 4: "W4_ERR_ALIGN",
@@ -80,6 +83,8 @@ SIGNATURES = {
     "w4_dequant_fp4": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _vp]),
     "w4_int4_gemv_operands": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _vp]),
     "w4_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
+    "w4_tune_param": (_i32, [_i32, _i32, _i32, _i32]),
+    "w4_tune_force": (_i32, [_i32, _i32]),
 }
 
 READ_PROBE_SINK = 4096
@@ -418,3 +423,26 @@ def w4_read_probe(src, sink, nbytes: int | None = None, stream=None) -> None:
     if n < 0 or n > total:
         raise ValueError(f"nbytes must lie in [0, {total}]")
     _check(lib.w4_read_probe(src.data_ptr(), n, sink.data_ptr(), _stream(stream)), "w4_read_probe")
+
+
+def w4_tune_param(kernel: str, M: int, K: int, N: int) -> int:
+    """The launch parameter a call of shape (M, K, N) of a kernel family uses (table, else rule)."""
+    return int(lib.w4_tune_param(TUNE_KERNELS[kernel], M, K, N))
+
+
+def w4_tune_force(kernel: str, param: int) -> None:
+    """Make every later call of a kernel family launch with ``param`` (0: back to the table)."""
+    _check(lib.w4_tune_force(TUNE_KERNELS[kernel], int(param)), "w4_tune_force")
+
+
+def w4_gemm_noalloc(x, qw, s, z, y, group: int = INT4_GROUP, stream=None) -> torch.Tensor:
+    """``w4_gemm`` for callers that cannot allocate: split-K partials in the library's per-GPU scratch."""
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    N, pq, ps, pz = _int4_weight(qw, s, z, K, group)
+    if tuple(y.shape) != (M, N):
+        raise ValueError(f"y must be [M, N] = {(M, N)}")
+    _check(lib.w4_gemm_noalloc(_dev(x, "x", _BF16), pq, ps, pz, _dev(y, "y", _BF16), M, K, N, group,
+                               _stream(stream)), "w4_gemm_noalloc")
+    return y

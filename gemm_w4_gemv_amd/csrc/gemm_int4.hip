@@ -38,17 +38,17 @@
 
 #include "w4.h"
 #include "w4_device.hpp"
+#include "tune.hpp"
 #include "w4_internal.hpp"
 
 namespace w4 {
 namespace {
 
-constexpr int kBM = 128, kBN = 64, kGroup = 128;
+constexpr int kBM = kGemmTileM, kBN = kGemmTileN, kGroup = 128;
 constexpr int kWaves = 16, kThreads = kWaves * kWave;
 constexpr int kRB = kBM / 16, kCB = kBN / 16;     // MFMA row and column blocks per tile
 constexpr int kNH = kWaves / 4, kCBW = kCB / kNH;  // column parts, column blocks per wave
 constexpr int kDepth = 2;                          // steps of global loads in flight in registers
-constexpr int kTargetBlocks = 256;                 // one workgroup per compute unit of an MI355X
 constexpr int kMaxGroups = W4_GEMM_MAX_K / kGroup;
 
 // LDS map (bytes).  During the K loop: two activation tiles, two weight
@@ -268,21 +268,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     y[i] = f32_to_bf16(t);
 }
 
-int choose_splits(int M, int K, int N) {
-    const long tiles = (long)((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-    const int G = K / kGroup;
-    int splits = (int)((kTargetBlocks + tiles / 2) / tiles);  // round(target / tiles)
-    if (splits < 1) splits = 1;
-    if (splits > G) splits = G;
-    if (splits > 16) splits = 16;
-    return splits;
-}
 
 }  // namespace
 
 size_t gemm_int4_workspace_bytes(int M, int K, int N) {
     if (M <= kGemmSmallMMax || N <= 0 || K <= 0 || K % kGroup != 0 || K > W4_GEMM_MAX_K) return 0;
-    const int splits = choose_splits(M, K, N);
+    const int splits = gemm_splits(M, K, N);
     return splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
@@ -295,7 +286,7 @@ hipError_t launch_gemm_int4(const void* x, const int32_t* qw, const void* s, con
     // Two rows: still a GEMV, each unpacked word shared by both rows.
     if (gemv_rows_int4_supports(M, K)) return launch_gemv_rows_int4(x, qw, s, z, y, M, K, N, stream);
     if (M <= kGemmSmallMMax) return launch_gemm_int4_small_m(x, qw, s, z, y, M, K, N, stream);
-    const int splits = choose_splits(M, K, N);
+    const int splits = gemm_splits(M, K, N);
     const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM), (unsigned)splits);
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const uint32_t* wb = reinterpret_cast<const uint32_t*>(qw);

@@ -35,6 +35,7 @@
 
 #include "w4.h"
 #include "w4_device.hpp"
+#include "tune.hpp"
 #include "w4_internal.hpp"
 
 namespace w4 {
@@ -250,19 +251,19 @@ hipError_t launch_gemm_int4_small_m(const void* x, const int32_t* qw, const void
     const uint16_t* sb = static_cast<const uint16_t*>(s);
     const uint16_t* zb = static_cast<const uint16_t*>(z);
     uint16_t* yb = static_cast<uint16_t*>(y);
-    // The widest tile (64, 32 or 16 weight rows) that still gives at least
-    // 240 workgroups: wider tiles read the activations fewer times.  Asking
-    // for at least 480 or 960 workgroups instead was slower on K3840 ->
-    // N15360 (16.6-18.8 / 19.6-23.7 us at M = 4-16, against 15.9-16.8).
+    // Weight rows per workgroup (16 per block) from the per-shape table, else
+    // the widest tile that still gives 240 workgroups (the rule in tune.hip).
     auto launch = [&](auto cb) {
         constexpr int kCB = decltype(cb)::value;
         const dim3 grid((unsigned)((N + 16 * kCB - 1) / (16 * kCB)));
         gemm_int4_small_m_kernel<kCB><<<grid, kThreads, 0, stream>>>(xb, wb, sb, zb, yb, M, K, N);
         return hipGetLastError();
     };
-    if ((N + 63) / 64 >= 240) return launch(std::integral_constant<int, 4>{});
-    if ((N + 31) / 32 >= 240) return launch(std::integral_constant<int, 2>{});
-    return launch(std::integral_constant<int, 1>{});
+    switch (gemm_small_m_blocks(M, K, N)) {
+        case 4: return launch(std::integral_constant<int, 4>{});
+        case 2: return launch(std::integral_constant<int, 2>{});
+        default: return launch(std::integral_constant<int, 1>{});
+    }
 }
 
 }  // namespace w4

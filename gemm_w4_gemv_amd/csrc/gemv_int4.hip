@@ -24,16 +24,8 @@
 //     waves that split one row (long K) combine through LDS in a fixed
 //     order.  No atomics: results are bit-reproducible.
 #include "gemv_common.hpp"
+#include "tune.hpp"
 #include "w4_internal.hpp"
-
-// Rows per wave are the most (8, 4, 2, 1) that still launch at least this
-// many workgroups: fewer, larger workgroups cost less per launch, more of
-// them keep more loads in flight.  Measured on the decode shapes: 256 suits
-// GEMVs under 16 MB of weights (3840 x 3840: 4.2 us instead of 4.8 at 1024),
-// 512 the larger ones (3840 -> 15360: 8.6 us instead of 8.9).
-constexpr int kMinBlocksSmall = 256;
-constexpr int kMinBlocksLarge = 512;
-constexpr size_t kSmallWeightBytes = (size_t)16 << 20;
 
 namespace w4 {
 namespace {
@@ -151,16 +143,16 @@ hipError_t launch_shape(const void* x, const int32_t* qw, const void* s, const v
     return hipGetLastError();
 }
 
+// Rows per wave from the per-shape table (else the rule in tune.hip).
 template <int S, int CPL>
 hipError_t launch_rpt(const void* x, const int32_t* qw, const void* s, const void* z, void* y,
                       int C, int N, hipStream_t stream) {
-    constexpr int T = 4 / S;
-    auto blocks = [&](int rpt) { return (N + T * rpt - 1) / (T * rpt); };
-    const int min_blocks = (size_t)N * (size_t)C * 16u < kSmallWeightBytes ? kMinBlocksSmall : kMinBlocksLarge;
-    if (blocks(8) >= min_blocks) return launch_shape<S, CPL, 8>(x, qw, s, z, y, C, N, stream);
-    if (blocks(4) >= min_blocks) return launch_shape<S, CPL, 4>(x, qw, s, z, y, C, N, stream);
-    if (blocks(2) >= min_blocks) return launch_shape<S, CPL, 2>(x, qw, s, z, y, C, N, stream);
-    return launch_shape<S, CPL, 1>(x, qw, s, z, y, C, N, stream);
+    switch (gemv_rows_per_wave(C * 32, N)) {
+        case 8: return launch_shape<S, CPL, 8>(x, qw, s, z, y, C, N, stream);
+        case 4: return launch_shape<S, CPL, 4>(x, qw, s, z, y, C, N, stream);
+        case 2: return launch_shape<S, CPL, 2>(x, qw, s, z, y, C, N, stream);
+        default: return launch_shape<S, CPL, 1>(x, qw, s, z, y, C, N, stream);
+    }
 }
 
 }  // namespace

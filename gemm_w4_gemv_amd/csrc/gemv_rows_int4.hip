@@ -24,13 +24,13 @@
 //     21-23 us, 1 row: 30-33 us: fewer loads in flight), so M >= 3 stays
 //     there.
 #include "gemv_common.hpp"
+#include "tune.hpp"
 #include "w4_internal.hpp"
 
 namespace w4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMinBlocks = 512;
 
 // sum over the chunk's 32 codes of (128 + q) * x_m for each of MX rows of x,
 // the codes unpacked once.
@@ -176,15 +176,15 @@ hipError_t launch_shape(const void* x, const int32_t* qw, const void* s, const v
     return hipGetLastError();
 }
 
-// Rows per wave: the most (4, 2, 1) that still launch kMinBlocks workgroups.
+// Rows per wave from the per-shape table (else the rule in tune.hip).
 template <int S, int CPL, int MX>
 hipError_t launch_rpt(const void* x, const int32_t* qw, const void* s, const void* z, void* y, int M, int C,
                       int N, hipStream_t stream) {
-    constexpr int T = 4 / S;
-    auto blocks = [&](int rpt) { return (N + T * rpt - 1) / (T * rpt); };
-    if (blocks(4) >= kMinBlocks) return launch_shape<S, CPL, 4, MX>(x, qw, s, z, y, M, C, N, stream);
-    if (blocks(2) >= kMinBlocks) return launch_shape<S, CPL, 2, MX>(x, qw, s, z, y, M, C, N, stream);
-    return launch_shape<S, CPL, 1, MX>(x, qw, s, z, y, M, C, N, stream);
+    switch (gemv_rows2_rows_per_wave(C * 32, N)) {
+        case 4: return launch_shape<S, CPL, 4, MX>(x, qw, s, z, y, M, C, N, stream);
+        case 2: return launch_shape<S, CPL, 2, MX>(x, qw, s, z, y, M, C, N, stream);
+        default: return launch_shape<S, CPL, 1, MX>(x, qw, s, z, y, M, C, N, stream);
+    }
 }
 
 template <int MX>

@@ -15,11 +15,9 @@
 // outside the pool turns that slot's outputs into NaN without touching any
 // weight.
 #include "w4_device.hpp"
+#include "tune.hpp"
 #include "w4_internal.hpp"
 
-#ifndef W4_MOE_MIN_BLOCKS
-#define W4_MOE_MIN_BLOCKS 512  // launch at least this many workgroups when N allows (256-512 measured best for the 6-slot FCs)
-#endif
 
 namespace w4 {
 namespace {
@@ -150,17 +148,16 @@ hipError_t launch_shape(const void* x, int64_t x_stride, const uint8_t* qw, cons
     return hipGetLastError();
 }
 
+// Rows per wave from the per-shape table (else the rule in tune.hip).
 template <int S, int CPL>
 hipError_t launch_rpt(const void* x, int64_t x_stride, const uint8_t* qw, const void* s,
                       const int32_t* ids, void* y, int E, int num_experts, int C, int N,
                       hipStream_t stream) {
-    constexpr int T = 4 / S;
-    auto blocks = [&](int rpt) { return (long)E * ((N + T * rpt - 1) / (T * rpt)); };
-    if (blocks(4) >= W4_MOE_MIN_BLOCKS)
-        return launch_shape<S, CPL, 4>(x, x_stride, qw, s, ids, y, E, num_experts, C, N, stream);
-    if (blocks(2) >= W4_MOE_MIN_BLOCKS)
-        return launch_shape<S, CPL, 2>(x, x_stride, qw, s, ids, y, E, num_experts, C, N, stream);
-    return launch_shape<S, CPL, 1>(x, x_stride, qw, s, ids, y, E, num_experts, C, N, stream);
+    switch (moe_gemv_rows_per_wave(E, C * 32, N)) {
+        case 4: return launch_shape<S, CPL, 4>(x, x_stride, qw, s, ids, y, E, num_experts, C, N, stream);
+        case 2: return launch_shape<S, CPL, 2>(x, x_stride, qw, s, ids, y, E, num_experts, C, N, stream);
+        default: return launch_shape<S, CPL, 1>(x, x_stride, qw, s, ids, y, E, num_experts, C, N, stream);
+    }
 }
 
 }  // namespace

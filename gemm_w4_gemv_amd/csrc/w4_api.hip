@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "chain.hpp"
+#include "tune.hpp"
 #include "w4.h"
 #include "w4_internal.hpp"
 
@@ -164,6 +165,25 @@ W4_API w4_status w4_gemm_noalloc(const void* x, const int32_t* qw, const void* s
     }
     hipError_t err = w4::launch_gemm_int4(x, qw, s, z, y, M, K, N, scratch, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? W4_OK : hip_fail(err, fn);
+}
+
+W4_API int w4_tune_param(int kernel, int M, int K, int N) {
+    switch (kernel) {
+        case W4_TUNE_GEMV: return w4::gemv_rows_per_wave(K, N);
+        case W4_TUNE_GEMV_ROWS2: return w4::gemv_rows2_rows_per_wave(K, N);
+        case W4_TUNE_GEMM_SMALL_M: return w4::gemm_small_m_blocks(M, K, N);
+        case W4_TUNE_GEMM: return w4::gemm_splits(M, K, N);
+        case W4_TUNE_MOE_GEMV: return w4::moe_gemv_rows_per_wave(M, K, N);
+        default: return -1;
+    }
+}
+
+W4_API w4_status w4_tune_force(int kernel, int param) {
+    if (kernel < 0 || kernel >= W4_TUNE_KERNELS) return fail(W4_ERR_ARG, "w4_tune_force: unknown kernel %d", kernel);
+    if (param != 0 && !w4::tune_param_valid(kernel, param))
+        return fail(W4_ERR_ARG, "w4_tune_force: %d is not a launch parameter of kernel %d", param, kernel);
+    w4::tune_force(kernel, param);
+    return W4_OK;
 }
 
 W4_API w4_status w4_moe_gemv(const void* x, int64_t x_stride, const uint8_t* qw_fp4, const void* s_fp4,

@@ -14,6 +14,8 @@ hipError_t launch_gemv_int4(const void* x, const int32_t* qw, const void* s, con
                             void* y, int K, int N, hipStream_t stream);
 
 size_t gemm_int4_workspace_bytes(int M, int K, int N);
+// Output tile of the prefill GEMM's workgroup (rows of x, weight rows).
+constexpr int kGemmTileM = 128, kGemmTileN = 64;
 // Small-M path of w4_gemm (M <= kGemmSmallMMax): one matrix-core block of 16
 // x rows against the weights, streamed once, no workspace.  Measured on the
 // decode shapes (us, small-M path vs the tiled GEMM): M = 16: 16.8 vs 23.0

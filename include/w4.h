@@ -213,6 +213,34 @@ W4_API w4_status w4_moe_gemm(const void* x, const int32_t* row_start, const int3
                              int max_rows, int num_experts, int K, int N, void* stream);
 
 /*
+ * Launch tuning.  Each kernel family has one launch parameter; its value for
+ * a call comes from a table of choices measured on an MI355X for the
+ * workloads' shapes ("Lab 5: Gemma4 端到端推理优化", section "GEMV 分块测试":
+ * the GEMV block shape was chosen per workload by a sweep), else from the
+ * launcher's rule.  Every value computes the same operation; summation order
+ * (and so the last bits) may differ between values, never between runs.
+ *   W4_TUNE_GEMV          w4_gemv, w4_gemm at M = 1: weight rows per wave, 1, 2, 4 or 8
+ *   W4_TUNE_GEMV_ROWS2    w4_gemm at M = 2 (K <= 16384): weight rows per wave, 1, 2 or 4
+ *   W4_TUNE_GEMM_SMALL_M  w4_gemm at 3 <= M <= 16: weight rows per workgroup / 16, 1, 2 or 4
+ *   W4_TUNE_GEMM          w4_gemm at M > 16: K splits, 1 .. 16 (at most K / 128); it sets
+ *                         w4_gemm_workspace_bytes()
+ *   W4_TUNE_MOE_GEMV      w4_moe_gemv: weight rows per wave, 1, 2 or 4 (M = the slot count E)
+ * w4_tune_param returns the parameter a call of shape (M, K, N) would launch
+ * with, or -1 for an unknown kernel.  w4_tune_force makes every later call of
+ * a kernel family launch with ``param`` (0 restores the table), for tuning
+ * sweeps and tests; it is process-wide and must not race with calls.
+ * Errors (w4_tune_force): W4_ERR_ARG (unknown kernel or parameter).
+ */
+#define W4_TUNE_GEMV 0
+#define W4_TUNE_GEMV_ROWS2 1
+#define W4_TUNE_GEMM_SMALL_M 2
+#define W4_TUNE_GEMM 3
+#define W4_TUNE_MOE_GEMV 4
+#define W4_TUNE_KERNELS 5
+W4_API int w4_tune_param(int kernel, int M, int K, int N);
+W4_API w4_status w4_tune_force(int kernel, int param);
+
+/*
  * Decode-step graphs.  "Lab 5: Gemma4 端到端推理优化", section "CUDA Graph":
  * the whole decode step is captured once and replayed once per token, which
  * needs static buffers.  w4_graph_begin starts capturing ``stream`` (which

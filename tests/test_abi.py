@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 25, names
     for name in names:
         assert hasattr(lib, name), f"libw4.so does not export {name}"
         assert name in w4.SIGNATURES, f"binding has no signature for {name}"
@@ -262,3 +262,61 @@ def test_chain_validation():
     assert lib.w4_chain_create((w4.GemvDesc * 1)(desc()), 0, WSP, 1 << 20, ctypes.byref(h)) == ARG
     assert lib.w4_chain_run(None, None) == ARG
     lib.w4_chain_destroy(None)
+
+
+# ------------------------------------------------------------- launch tuning
+TABLE = ROOT / "gemm_w4_gemv_amd" / "csrc" / "tune_table.inc"
+TUNE_IDS = {"W4_TUNE_GEMV": 0, "W4_TUNE_GEMV_ROWS2": 1, "W4_TUNE_GEMM_SMALL_M": 2, "W4_TUNE_GEMM": 3,
+            "W4_TUNE_MOE_GEMV": 4}
+
+
+def table_entries():
+    rows = re.findall(r"\{(W4_TUNE_\w+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+)\}", TABLE.read_text())
+    return [(TUNE_IDS[k], int(m), int(kk), int(n), int(p)) for k, m, kk, n, p in rows]
+
+
+def test_tune_ids_match_header():
+    text = HEADER.read_text()
+    for name, i in TUNE_IDS.items():
+        assert f"#define {name} {i}" in text
+    assert sorted(w4.TUNE_KERNELS.values()) == sorted(TUNE_IDS.values())
+
+
+def test_tune_table_drives_the_launchers():
+    """Every measured entry is what the launchers use for its shape."""
+    entries = table_entries()
+    assert entries, "the tuning table is empty"
+    for kernel, M, K, N, param in entries:
+        assert lib.w4_tune_param(kernel, M if M else 1, K, N) == param, (kernel, M, K, N)
+
+
+def test_tune_rules_outside_the_table():
+    # the rules: GEMV rows per wave, small-M width, prefill K splits, FP4 GEMV rows per wave
+    assert lib.w4_tune_param(0, 1, 256, 7) == 1
+    assert lib.w4_tune_param(0, 1, 4096, 1 << 20) == 8
+    assert lib.w4_tune_param(2, 4, 256, 130) == 1
+    assert lib.w4_tune_param(2, 4, 256, 64 * 240) == 4
+    assert lib.w4_tune_param(3, 128, 2048, 64) == 16  # one tile: 16 splits (= K / 128)
+    assert lib.w4_tune_param(3, 128, 256, 64) == 2   # at most one group per split
+    assert lib.w4_tune_param(3, 1024, 3840, 1 << 14) == 1
+    assert lib.w4_tune_param(4, 6, 256, 1 << 16) == 4
+    assert lib.w4_tune_param(9, 1, 256, 64) == -1
+
+
+def test_tune_force_and_reset():
+    assert lib.w4_tune_force(5, 1) == ARG
+    assert lib.w4_tune_force(-1, 1) == ARG
+    assert lib.w4_tune_force(0, 3) == ARG
+    assert lib.w4_tune_force(3, 17) == ARG
+    before = lib.w4_tune_param(3, 128, 2048, 64)
+    try:
+        assert lib.w4_tune_force(3, 5) == OK
+        assert lib.w4_tune_param(3, 128, 2048, 64) == 5
+        assert lib.w4_tune_param(3, 128, 256, 64) == 2  # still at most one group per split
+        assert lib.w4_gemm_workspace_bytes(128, 2048, 64, 128) == 5 * 128 * 64 * 4
+        assert lib.w4_tune_force(0, 8) == OK
+        assert lib.w4_tune_param(0, 1, 3840, 3840) == 8
+    finally:
+        assert lib.w4_tune_force(3, 0) == OK
+        assert lib.w4_tune_force(0, 0) == OK
+    assert lib.w4_tune_param(3, 128, 2048, 64) == before
