@@ -27,7 +27,7 @@ __all__ = [
     "w4_dequant_int4", "w4_dequant_fp4", "w4_int4_gemv_operands", "INT4_GROUP", "FP4_GROUP", "GEMV_MAX_K",
     "GemvDesc", "W4Chain", "w4_chain_workspace_bytes", "w4_chain_create", "w4_chain_run",
     "w4_chain_error", "w4_chain_destroy", "CHAIN_MAX_K", "w4_read_probe", "READ_PROBE_SINK",
-    "w4_tune_param", "w4_tune_force", "TUNE_KERNELS", "w4_gemm_noalloc",
+    "w4_tune_param", "w4_tune_force", "TUNE_KERNELS", "w4_gemm_noalloc", "w4_repack_gptq",
 ]
 
 # W4_LIBRARY names another build of the same library (the chain-timeline build
@@ -84,6 +84,7 @@ SIGNATURES = {
     "w4_int4_gemv_operands": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _vp]),
     "w4_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
     "w4_tune_param": (_i32, [_i32, _i32, _i32, _i32]),
+    "w4_repack_gptq": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
     "w4_tune_force": (_i32, [_i32, _i32]),
 }
 
@@ -446,3 +447,20 @@ def w4_gemm_noalloc(x, qw, s, z, y, group: int = INT4_GROUP, stream=None) -> tor
     _check(lib.w4_gemm_noalloc(_dev(x, "x", _BF16), pq, ps, pz, _dev(y, "y", _BF16), M, K, N, group,
                                _stream(stream)), "w4_gemm_noalloc")
     return y
+
+
+def w4_repack_gptq(qweight, s_gn, z_gn, group: int = INT4_GROUP, stream=None):
+    """GPTQ's K-major layout (int32 ``[K/8, N]``, fp16 ``[K/128, N]``) -> new device tensors
+    ``qw [N, K/8]``, ``s``, ``z [N, K/128]`` in the layout the other entry points read."""
+    if not (isinstance(qweight, torch.Tensor) and qweight.dtype == torch.int32 and qweight.dim() == 2):
+        raise ValueError("qweight must be an int32 [K/8, N] tensor")
+    K, N = qweight.shape[0] * 8, qweight.shape[1]
+    for name, t in (("s_gn", s_gn), ("z_gn", z_gn)):
+        if tuple(t.shape) != (K // group, N):
+            raise ValueError(f"{name} must be [K/{group}, N] = {(K // group, N)}")
+    qw = torch.empty(N, K // 8, dtype=torch.int32, device=qweight.device)
+    s = torch.empty(N, K // group, dtype=torch.float16, device=qweight.device)
+    z = torch.empty_like(s)
+    _check(lib.w4_repack_gptq(_dev(qweight, "qweight", _I32), _dev(s_gn, "s_gn", _F16), _dev(z_gn, "z_gn", _F16),
+                              qw.data_ptr(), s.data_ptr(), z.data_ptr(), K, N, group, _stream(stream)), "w4_repack_gptq")
+    return qw, s, z

@@ -186,6 +186,30 @@ W4_API w4_status w4_tune_force(int kernel, int param) {
     return W4_OK;
 }
 
+W4_API w4_status w4_repack_gptq(const int32_t* qw_kn, const void* s_gn, const void* z_gn, int32_t* qw, void* s,
+                                void* z, int K, int N, int g, void* stream) {
+    const char* fn = "w4_repack_gptq";
+    if (!qw_kn || !s_gn || !z_gn || !qw || !s || !z) return fail(W4_ERR_NULL, "%s: no pointer may be NULL", fn);
+    if (g != W4_INT4_GROUP) return fail(W4_ERR_UNSUPPORTED, "%s: group size %d (only 128 is supported)", fn, g);
+    if (N < 0) return fail(W4_ERR_SHAPE, "%s: N = %d is negative", fn, N);
+    if (K <= 0 || K % g != 0) return fail(W4_ERR_SHAPE, "%s: K = %d is not a positive multiple of %d", fn, K, g);
+    if (!aligned(qw_kn, 4) || !aligned(qw, 4) || !aligned(s_gn, 2) || !aligned(z_gn, 2) || !aligned(s, 2) ||
+        !aligned(z, 2))
+        return fail(W4_ERR_ALIGN, "%s: packed words must be 4-byte, scales and zeros 2-byte aligned", fn);
+    const size_t wb = (size_t)N * K / 2, sb = (size_t)N * (K / g) * 2;
+    const Range ins[3] = {range(qw_kn, wb), range(s_gn, sb), range(z_gn, sb)};
+    const Range outs[3] = {range(qw, wb), range(s, sb), range(z, sb)};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 3; ++j)
+            if (overlap(outs[i], ins[j])) return fail(W4_ERR_ALIAS, "%s: an output overlaps an input", fn);
+        for (int j = 0; j < i; ++j)
+            if (overlap(outs[i], outs[j])) return fail(W4_ERR_ALIAS, "%s: two outputs overlap", fn);
+    }
+    if (N == 0) return W4_OK;
+    hipError_t err = w4::launch_repack_gptq(qw_kn, s_gn, z_gn, qw, s, z, K, N, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4_OK : hip_fail(err, fn);
+}
+
 W4_API w4_status w4_moe_gemv(const void* x, int64_t x_stride, const uint8_t* qw_fp4, const void* s_fp4,
                              const int32_t* expert_ids, void* y, int E, int num_experts, int K, int N,
                              void* stream) {

@@ -51,6 +51,9 @@ hipError_t launch_int4_gemv_operands(const int32_t* qw, const void* x, uint32_t*
 hipError_t launch_dequant_fp4(const uint8_t* qw, const void* s, float* out_f32, void* out_bf16,
                               int K, int N, hipStream_t stream);
 
+hipError_t launch_repack_gptq(const int32_t* qw_kn, const void* s_gn, const void* z_gn, int32_t* qw, void* s, void* z,
+                              int K, int N, hipStream_t stream);
+
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int sink_words, hipStream_t stream);
 
 // Split of the K range of a GEMV row over the four waves of a workgroup.

@@ -213,6 +213,24 @@ W4_API w4_status w4_moe_gemm(const void* x, const int32_t* row_start, const int3
                              int max_rows, int num_experts, int K, int N, void* stream);
 
 /*
+ * w4_repack_gptq -- import a weight stored in GPTQ's own K-major layout
+ * ("Lab 5: Gemma4 端到端推理优化", section "量化正确性": GPTQ INT4, group 128,
+ * asymmetric), once, at load time, into the layout every other entry point
+ * reads:
+ *   qw_kn  device int32 [K/8][N]: word (p, n) holds the codes of k = 8p .. 8p+7
+ *          of output n, nibble j (bits 4j .. 4j+3) for k = 8p + j
+ *   s_gn, z_gn  device fp16 [K/g][N]
+ * into qw int32 [N][K/8], s and z fp16 [N][K/g] (a transpose of words and of
+ * 16-bit values; every code keeps its nibble position).  Inputs are not
+ * modified; outputs must not overlap inputs or each other.  Packed words
+ * 4-byte aligned, scales and zeros 2-byte aligned; K a positive multiple of
+ * g = 128; N >= 0.  Asynchronous on ``stream``; capturable.
+ * Errors: W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_UNSUPPORTED, W4_ERR_ALIGN, W4_ERR_ALIAS, W4_ERR_HIP.
+ */
+W4_API w4_status w4_repack_gptq(const int32_t* qw_kn, const void* s_gn, const void* z_gn, int32_t* qw,
+                                void* s, void* z, int K, int N, int g, void* stream);
+
+/*
  * Launch tuning.  Each kernel family has one launch parameter; its value for
  * a call comes from a table of choices measured on an MI355X for the
  * workloads' shapes ("Lab 5: Gemma4 端到端推理优化", section "GEMV 分块测试":

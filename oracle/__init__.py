@@ -47,6 +47,7 @@ __all__ = [
     "f16_to_f64", "bf16_to_f64", "int4_codes", "dequant_int4", "e2m1_value",
     "fp4_codes", "dequant_fp4", "linear", "gemv_int4", "gemm_int4",
     "moe_gemv_fp4", "moe_gemm_fp4", "round_bf16", "bf16_bits", "INT4_GROUP", "FP4_GROUP",
+    "gptq_codes", "repack_gptq",
 ]
 
 
@@ -89,6 +90,33 @@ def dequant_int4(qw, s_bits, z_bits, group: int = INT4_GROUP) -> np.ndarray:
     z = np.repeat(f16_to_f64(z_bits), group, axis=1)
     assert s.shape == q.shape and z.shape == q.shape, "scale/zero shape does not match K/group"
     return (q - z) * s
+
+
+def gptq_codes(qweight) -> np.ndarray:
+    """Codes ``uint8 [N, K]`` of a weight in GPTQ's own K-major layout.
+
+    Lab 5, "量化正确性": the weights are GPTQ INT4.  GPTQ keeps the packed codes
+    K-major, ``qweight int32 [K/8, N]``: word ``(p, n)`` holds the codes of
+    ``k = 8p .. 8p+7`` of output ``n``, nibble ``j`` for ``k = 8p + j`` (the same
+    nibble order as reading 2); its scales and zeros are ``[K/128, N]``.
+    """
+    w = np.asarray(qweight).view(np.uint32)
+    kw, n = w.shape
+    shifts = (4 * np.arange(8, dtype=np.uint32))[None, None, :]
+    codes = (w.T[:, :, None] >> shifts) & np.uint32(0xF)  # [N, K/8, 8]
+    return codes.reshape(n, kw * 8).astype(np.uint8)
+
+
+def repack_gptq(qweight, s_gn, z_gn):
+    """GPTQ's layout -> this path's ``F.linear`` layout (reading 3): ``qw int32 [N, K/8]``
+    with nibble ``j`` of word ``(n, p)`` the code of ``k = 8p + j``, and scales and
+    zeros ``[N, K/128]``.  The codes are unpacked by their GPTQ definition and packed
+    again by this layout's, each code unchanged."""
+    codes = gptq_codes(qweight).astype(np.uint32)
+    n, k = codes.shape
+    shifts = (4 * np.arange(8, dtype=np.uint32))[None, None, :]
+    qw = np.bitwise_or.reduce(codes.reshape(n, k // 8, 8) << shifts, axis=2).astype(np.uint32).view(np.int32)
+    return qw, np.ascontiguousarray(np.asarray(s_gn).T), np.ascontiguousarray(np.asarray(z_gn).T)
 
 
 # ----------------------------------------------------------------------- FP4

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 25, names
+    assert len(names) == 26, names
     for name in names:
         assert hasattr(lib, name), f"libw4.so does not export {name}"
         assert name in w4.SIGNATURES, f"binding has no signature for {name}"
@@ -320,3 +320,15 @@ def test_tune_force_and_reset():
         assert lib.w4_tune_force(3, 0) == OK
         assert lib.w4_tune_force(0, 0) == OK
     assert lib.w4_tune_param(3, 128, 2048, 64) == before
+
+
+def test_repack_gptq_validation():
+    rp = lib.w4_repack_gptq
+    assert rp(None, S, Z, QW, WSP, Y, 256, 64, 128, None) == NULL
+    assert rp(X, S, Z, QW, WSP, Y, 200, 64, 128, None) == SHAPE
+    assert rp(X, S, Z, QW, WSP, Y, 256, -1, 128, None) == SHAPE
+    assert rp(X, S, Z, QW, WSP, Y, 256, 64, 64, None) == UNSUP
+    assert rp(X + 2, S, Z, QW, WSP, Y, 256, 64, 128, None) == ALIGN
+    assert rp(X, S, Z, X + 64, WSP, Y, 256, 64, 128, None) == ALIAS  # qw over qw_kn
+    assert rp(X, S, Z, QW, QW + 64, Y, 256, 64, 128, None) == ALIAS  # s over qw
+    assert rp(X, S, Z, QW, WSP, Y, 256, 0, 128, None) == OK  # empty: nothing launched

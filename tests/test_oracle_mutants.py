@@ -103,6 +103,17 @@ def _dequant_fp4_scale_by_k(qw, s_bits, group=32):
     return v * s[..., idx]
 
 
+def _repack_reshaped_not_transposed(qweight, s_gn, z_gn):
+    qw = np.ascontiguousarray(np.asarray(qweight).reshape(np.asarray(qweight).shape[::-1]))
+    return qw, np.ascontiguousarray(np.asarray(s_gn).T), np.ascontiguousarray(np.asarray(z_gn).T)
+
+
+def _gptq_codes_nibbles_reversed(qweight):
+    c = _orig["gptq_codes"](qweight)
+    n, k = c.shape
+    return c.reshape(n, k // 8, 8)[:, :, ::-1].reshape(n, k)
+
+
 MUTANTS = {
     "reversed_int4_nibbles": ("int4_codes", _reversed_nibbles),
     "swapped_fp4_nibbles": ("fp4_codes", _swapped_fp4),
@@ -118,6 +129,8 @@ MUTANTS = {
     "moe_gemm_group_boundary_off_by_one": ("moe_gemm_fp4", _moe_gemm_group_shifted),
     "moe_gemm_ids_ignored": ("moe_gemm_fp4", _moe_gemm_ids_ignored),
     "gemv_row_chunks_shifted": ("gemv_int4", _gemv_chunks_shifted),
+    "gptq_repack_reshaped": ("repack_gptq", _repack_reshaped_not_transposed),
+    "gptq_nibbles_reversed": ("gptq_codes", _gptq_codes_nibbles_reversed),
 }
 
 

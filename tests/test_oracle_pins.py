@@ -367,3 +367,42 @@ def test_generator_distributions():
     pool = fp4_pool(0, (9,), 4, 4096, 16)
     sv = oracle.bf16_to_f64(pool["s"])
     assert sv.min() >= 2.0 ** -8 * 0.99 and sv.max() <= 2.0 ** -2 * 1.01
+
+
+# ------------------------------------------------------------ GPTQ layout
+def test_gptq_layout_literal_words():
+    """GPTQ's K-major words: column n's codes run down the word rows.  Column 0
+    holds 0..7 then F..8, column 1 holds 8..F then 7..0, so the repacked rows
+    are those literal words side by side."""
+    qweight = np.array([[0x76543210, 0xFEDCBA98],
+                        [0x89ABCDEF, 0x01234567]], dtype=np.uint32).view(np.int32)
+    codes = oracle.gptq_codes(qweight)
+    assert codes.tolist() == [list(range(8)) + list(range(15, 7, -1)),
+                              list(range(8, 16)) + list(range(7, -1, -1))]
+    s = f16_bits([[0.5, 0.25]])
+    z = f16_bits([[3.0, 9.0]])
+    qw, s2, z2 = oracle.repack_gptq(qweight, s, z)
+    assert qw.view(np.uint32).tolist() == [[0x76543210, 0x89ABCDEF], [0xFEDCBA98, 0x01234567]]
+    assert s2.tolist() == [[s[0, 0]], [s[0, 1]]] and z2.tolist() == [[z[0, 0]], [z[0, 1]]]
+
+
+def test_gptq_repack_keeps_every_code_and_the_product():
+    """Random GPTQ-layout weights: the repacked codes are the GPTQ codes (checked
+    against an independent packer, Python integers), and the product is the one
+    written from the GPTQ layout's definition."""
+    K, N = 256, 5
+    g = rng(41, 0)
+    codes = g.integers(0, 16, (N, K))
+    qweight = np.zeros((K // 8, N), dtype=np.uint32)
+    for n in range(N):
+        for k in range(K):
+            qweight[k // 8, n] |= int(codes[n, k]) << (4 * (k % 8))
+    qweight = qweight.view(np.int32)
+    s = f16_bits(g.uniform(0.002, 0.02, (K // 128, N)))
+    z = f16_bits(g.integers(0, 16, (K // 128, N)).astype(np.float64))
+    assert np.array_equal(oracle.gptq_codes(qweight), codes)
+    qw, s2, z2 = oracle.repack_gptq(qweight, s, z)
+    assert np.array_equal(qw, pack_int4(codes.astype(np.uint8)))
+    x = bf16_normal(41, (1,), (K,))
+    W = (codes - np.repeat(oracle.f16_to_f64(z).T, 128, axis=1)) * np.repeat(oracle.f16_to_f64(s).T, 128, axis=1)
+    assert np.allclose(oracle.gemv_int4(x, qw, s2, z2), W @ oracle.bf16_to_f64(x), rtol=0, atol=1e-12)
