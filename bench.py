@@ -293,20 +293,31 @@ def extra_workloads(w4, host, si, torch, rf):
     y1 = torch.empty(si.MOE_SLOTS, N1, dtype=torch.bfloat16, device="cuda")
     y2 = torch.empty(si.MOE_SLOTS, N2, dtype=torch.bfloat16, device="cuda")
 
-    def moe_tokens():
+    def moe_tokens():  # one launch per token: FC1 and FC2 together (w4_moe_gemv2)
+        for t in range(tokens):
+            w4.w4_moe_gemv2((x1, pools[0]["qw"], pools[0]["s"], y1), (x2, pools[1]["qw"], pools[1]["s"], y2),
+                            ids[t], stream=stream)
+
+    def moe_tokens_two():  # two launches per token
         for t in range(tokens):
             w4.w4_moe_gemv(x1, pools[0]["qw"], pools[0]["s"], ids[t], y1, stream=stream)
             w4.w4_moe_gemv(x2, pools[1]["qw"], pools[1]["s"], ids[t], y2, stream=stream)
 
+    nb = rf.moe_bytes(si.MOE_SLOTS, K1, N1, True) + rf.moe_bytes(si.MOE_SLOTS, K2, N2, False)
     g = capture(w4, torch, stream, moe_tokens)
     ms = time_graph(torch, lambda: g.replay(stream), stream, reps=10)
-    us = ms * 1e3 / tokens
-    nb = rf.moe_bytes(si.MOE_SLOTS, K1, N1, True) + rf.moe_bytes(si.MOE_SLOTS, K2, N2, False)
+    g.destroy()
+    g = capture(w4, torch, stream, moe_tokens_two)
+    ms2 = time_graph(torch, lambda: g.replay(stream), stream, reps=10)
+    g.destroy()
+    us, us2 = ms * 1e3 / tokens, ms2 * 1e3 / tokens
     gbps = nb / (us * 1e-6) / 1e9
     out["moe_fp4_6x2fc"] = {"us_per_token": round(us, 2), "GBps": round(gbps, 1),
-                            "frac_hbm": round(gbps / rf.HBM_PEAK_GBPS, 4), "bytes_per_token": nb}
-    g.destroy()
-    log(f"FP4 MoE 6 experts x 2 FC: {us:.1f} us/token, {gbps:.0f} GB/s")
+                            "frac_hbm": round(gbps / rf.HBM_PEAK_GBPS, 4), "bytes_per_token": nb,
+                            "launches_per_token": 1,
+                            "two_launches_per_token": {"us_per_token": round(us2, 2),
+                                                       "GBps": round(nb / (us2 * 1e-6) / 1e9, 1)}}
+    log(f"FP4 MoE 6 experts x 2 FC: {us:.1f} us/token in one launch ({us2:.1f} in two), {gbps:.0f} GB/s")
 
     # grouped FP4 expert GEMM (w4_moe_gemm): 6 experts x 16 tokens each, FC1 then FC2,
     # a fresh id set per call (the same 64 id sets)
@@ -358,7 +369,11 @@ def cpu_baseline(si, rf, layers: int):
     out = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
            "sample": f"decode layers 0..{layers - 1}: {len(inputs)} linears, {nbytes} algorithmic bytes, "
                      f"{dt:.1f} s (FP64 numpy unpack + dequant + matmul)",
-           "seconds": round(dt, 2)}
+           "seconds": round(dt, 2),
+           "host_cores": len(os.sched_getaffinity(0)),
+           "threads_note": "cores = the BLAS threads available to the oracle's matrix-vector products; "
+                           "its unpack and dequantisation are single-threaded numpy, so the run is mostly "
+                           "one core (compare single_thread)"}
     # the same oracle on one thread, on layer 0 only
     try:
         from threadpoolctl import threadpool_limits

@@ -22,7 +22,7 @@ import torch
 
 __all__ = [
     "W4Error", "lib", "LIB_PATH", "w4_abi_version", "w4_status_string", "w4_last_error",
-    "w4_gemv", "w4_gemm", "w4_gemm_workspace_bytes", "w4_moe_gemv", "w4_moe_gemm",
+    "w4_gemv", "w4_gemm", "w4_gemm_workspace_bytes", "w4_moe_gemv", "w4_moe_gemv2", "w4_moe_gemm",
     "w4_graph_begin", "w4_graph_end", "w4_graph_replay", "w4_graph_destroy", "W4Graph",
     "w4_dequant_int4", "w4_dequant_fp4", "w4_int4_gemv_operands", "INT4_GROUP", "FP4_GROUP", "GEMV_MAX_K",
     "GemvDesc", "W4Chain", "w4_chain_workspace_bytes", "w4_chain_create", "w4_chain_run",
@@ -58,6 +58,12 @@ class GemvDesc(ctypes.Structure):
                 ("reserved", ctypes.c_int)]
 
 
+class MoeFc(ctypes.Structure):
+    """struct w4_moe_fc (include/w4.h)."""
+    _fields_ = [("x", ctypes.c_void_p), ("x_stride", ctypes.c_int64), ("qw_fp4", ctypes.c_void_p),
+                ("s_fp4", ctypes.c_void_p), ("y", ctypes.c_void_p), ("K", ctypes.c_int), ("N", ctypes.c_int)]
+
+
 # name -> (restype, argtypes), mirroring include/w4.h
 SIGNATURES = {
     "w4_abi_version": (_i32, []),
@@ -68,6 +74,7 @@ SIGNATURES = {
     "w4_gemm": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "w4_gemm_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "w4_moe_gemv": (_i32, [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "w4_moe_gemv2": (_i32, [ctypes.POINTER(MoeFc), ctypes.POINTER(MoeFc), _vp, _i32, _i32, _vp]),
     "w4_moe_gemm": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "w4_graph_begin": (_i32, [_vp]),
     "w4_graph_end": (_i32, [_vp, ctypes.POINTER(_vp)]),
@@ -247,6 +254,41 @@ def w4_moe_gemv(x, qw_fp4, s_fp4, expert_ids, y, stream=None) -> torch.Tensor:
                            _dev(expert_ids, "expert_ids", _I32), _dev(y, "y", _BF16), E, num_experts, K, N,
                            _stream(stream)), "w4_moe_gemv")
     return y
+
+
+def _moe_fc(x, qw_fp4, s_fp4, y, E):
+    if qw_fp4.dim() != 3:
+        raise ValueError("qw_fp4 must be [experts, N, K/2]")
+    num_experts, N, half_k = qw_fp4.shape
+    K = 2 * half_k
+    if tuple(s_fp4.shape) != (num_experts, N, K // FP4_GROUP):
+        raise ValueError(f"s_fp4 must be [experts, N, K/32]; got {tuple(s_fp4.shape)}")
+    if x.dim() == 1:
+        stride = 0
+        if x.numel() != K:
+            raise ValueError(f"x must have K = {K} values")
+    else:
+        if x.dim() != 2 or x.shape[1] != K or x.shape[0] < E:
+            raise ValueError(f"x must be [E, K] = {(E, K)}; got {tuple(x.shape)}")
+        stride = K
+    if tuple(y.shape) != (E, N):
+        raise ValueError(f"y must be [E, N] = {(E, N)}; got {tuple(y.shape)}")
+    fc = MoeFc(_dev(x, "x", _BF16), stride, _dev(qw_fp4, "qw_fp4", _U8), _dev(s_fp4, "s_fp4", _BF16),
+               _dev(y, "y", _BF16), K, N)
+    return fc, num_experts
+
+
+def w4_moe_gemv2(fc1, fc2, expert_ids, stream=None):
+    """Two FP4 expert FCs over the same slots in one launch; ``fc1`` and ``fc2`` are
+    ``(x, qw_fp4, s_fp4, y)`` as for ``w4_moe_gemv`` (their inputs must not depend on each other)."""
+    E = expert_ids.numel()
+    f1, n1 = _moe_fc(*fc1, E)
+    f2, n2 = _moe_fc(*fc2, E)
+    if n1 != n2:
+        raise ValueError("both expert pools must hold the same number of experts")
+    _check(lib.w4_moe_gemv2(ctypes.byref(f1), ctypes.byref(f2), _dev(expert_ids, "expert_ids", _I32), E, n1,
+                            _stream(stream)), "w4_moe_gemv2")
+    return fc1[3], fc2[3]
 
 
 class W4Graph:

@@ -40,19 +40,33 @@ __device__ __forceinline__ float chunk_dot(const u32x4_t w, const uint32_t xp[16
     return d0 + d1;
 }
 
-template <int S, int CPL, int RPT>
-__global__ __launch_bounds__(kThreads) void moe_gemv_fp4_kernel(
-    const u32x4_t* __restrict__ x, long x_stride_vec, const u32x4_t* __restrict__ qw,
-    const uint16_t* __restrict__ s, const int32_t* __restrict__ ids, uint16_t* __restrict__ y,
-    int C, int N, int num_experts) {
-    constexpr int T = 4 / S;
-    __shared__ float part[S][T * RPT];
+// One FC of expert GEMVs: slot e's x at x + e * x_stride_vec (16-byte
+// units), weights and scales of the pool, output y [E][N].
+struct MoeFc {
+    const u32x4_t* x;
+    long x_stride_vec;
+    const u32x4_t* qw;
+    const uint16_t* s;
+    uint16_t* y;
+    int C, N;
+};
 
-    const int slot = blockIdx.y;
+// Rows [bx T RPT, (bx + 1) T RPT) of slot ``slot``: the work of one workgroup.
+template <int S, int CPL, int RPT>
+__device__ __forceinline__ void moe_gemv_rows(const MoeFc& f, const int32_t* __restrict__ ids, int num_experts,
+                                              int bx, int slot, float (&part)[S][(4 / S) * RPT]) {
+    constexpr int T = 4 / S;
+    const u32x4_t* __restrict__ x = f.x;
+    const u32x4_t* __restrict__ qw = f.qw;
+    const uint16_t* __restrict__ s = f.s;
+    uint16_t* __restrict__ y = f.y;
+    const long x_stride_vec = f.x_stride_vec;
+    const int C = f.C, N = f.N;
+
     const int expert = ids[slot];
     if (expert < 0 || expert >= num_experts) {  // uniform across the workgroup
         if (threadIdx.x < T * RPT) {
-            const int row = blockIdx.x * (T * RPT) + threadIdx.x;
+            const int row = bx * (T * RPT) + threadIdx.x;
             if (row < N) y[(size_t)slot * N + row] = 0x7FC0u;  // bf16 quiet NaN
         }
         return;
@@ -80,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemv_fp4_kernel(
         for (int p = 0; p < 4; ++p) xraw[i][p] = xs[4 * c[i] + p];
     }
 
-    const int row0 = (blockIdx.x * T + team) * RPT;
+    const int row0 = (bx * T + team) * RPT;
     u32x4_t wv[RPT][CPL];
     uint16_t sraw[RPT][CPL];
 #pragma unroll
@@ -131,9 +145,29 @@ __global__ __launch_bounds__(kThreads) void moe_gemv_fp4_kernel(
         float t = 0.f;
 #pragma unroll
         for (int k = 0; k < S; ++k) t += part[k][threadIdx.x];
-        const int row = blockIdx.x * (T * RPT) + threadIdx.x;
+        const int row = bx * (T * RPT) + threadIdx.x;
         if (row < N) y[(size_t)slot * N + row] = f32_to_bf16(t);
     }
+}
+
+template <int S, int CPL, int RPT>
+__global__ __launch_bounds__(kThreads) void moe_gemv_fp4_kernel(MoeFc f, const int32_t* __restrict__ ids,
+                                                                int num_experts) {
+    __shared__ float part[S][(4 / S) * RPT];
+    moe_gemv_rows<S, CPL, RPT>(f, ids, num_experts, blockIdx.x, blockIdx.y, part);
+}
+
+// Two FCs over the same slots and expert ids in one launch: workgroups
+// [0, b1) of each slot run the first FC, the rest the second.  One launch
+// instead of two: the second FC's weights stream while the first's finish,
+// with one ramp and one tail.
+template <int CPL1, int CPL2, int RPT>
+__global__ __launch_bounds__(kThreads) void moe_gemv2_fp4_kernel(MoeFc f1, MoeFc f2, int b1,
+                                                                 const int32_t* __restrict__ ids,
+                                                                 int num_experts) {
+    __shared__ float part[1][4 * RPT];
+    if ((int)blockIdx.x < b1) moe_gemv_rows<1, CPL1, RPT>(f1, ids, num_experts, blockIdx.x, blockIdx.y, part);
+    else moe_gemv_rows<1, CPL2, RPT>(f2, ids, num_experts, blockIdx.x - b1, blockIdx.y, part);
 }
 
 template <int S, int CPL, int RPT>
@@ -142,9 +176,9 @@ hipError_t launch_shape(const void* x, int64_t x_stride, const uint8_t* qw, cons
                         hipStream_t stream) {
     constexpr int T = 4 / S;
     const dim3 grid((unsigned)((N + T * RPT - 1) / (T * RPT)), (unsigned)E);
-    moe_gemv_fp4_kernel<S, CPL, RPT><<<grid, kThreads, 0, stream>>>(
-        static_cast<const u32x4_t*>(x), (long)(x_stride / 8), reinterpret_cast<const u32x4_t*>(qw),
-        static_cast<const uint16_t*>(s), ids, static_cast<uint16_t*>(y), C, N, num_experts);
+    const MoeFc f{static_cast<const u32x4_t*>(x), (long)(x_stride / 8), reinterpret_cast<const u32x4_t*>(qw),
+                  static_cast<const uint16_t*>(s), static_cast<uint16_t*>(y), C, N};
+    moe_gemv_fp4_kernel<S, CPL, RPT><<<grid, kThreads, 0, stream>>>(f, ids, num_experts);
     return hipGetLastError();
 }
 
@@ -176,6 +210,50 @@ hipError_t launch_moe_gemv_fp4(const void* x, int64_t x_stride, const uint8_t* q
         case 4 * 16 + 4: return launch_rpt<4, 4>(x, x_stride, qw, s, ids, y, E, num_experts, C, N, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+namespace {
+
+template <int CPL1, int CPL2, int RPT>
+hipError_t launch_pair(const MoeFc& f1, const MoeFc& f2, const int32_t* ids, int E, int num_experts,
+                       hipStream_t stream) {
+    const int b1 = (f1.N + 4 * RPT - 1) / (4 * RPT), b2 = (f2.N + 4 * RPT - 1) / (4 * RPT);
+    moe_gemv2_fp4_kernel<CPL1, CPL2, RPT><<<dim3((unsigned)(b1 + b2), (unsigned)E), kThreads, 0, stream>>>(
+        f1, f2, b1, ids, num_experts);
+    return hipGetLastError();
+}
+
+template <int RPT>
+hipError_t launch_pair_rpt(const MoeFc& f1, const MoeFc& f2, const int32_t* ids, int E, int num_experts,
+                           hipStream_t stream) {
+    switch (row_split(f1.C).cpl * 16 + row_split(f2.C).cpl) {
+        case 1 * 16 + 1: return launch_pair<1, 1, RPT>(f1, f2, ids, E, num_experts, stream);
+        case 1 * 16 + 2: return launch_pair<1, 2, RPT>(f1, f2, ids, E, num_experts, stream);
+        case 2 * 16 + 1: return launch_pair<2, 1, RPT>(f1, f2, ids, E, num_experts, stream);
+        default: return launch_pair<2, 2, RPT>(f1, f2, ids, E, num_experts, stream);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_moe_gemv2_fp4(const MoeFcArgs& a, const MoeFcArgs& b, const int32_t* ids, int E, int num_experts,
+                                hipStream_t stream) {
+    // One launch when both rows fit one wave's slice (K <= 4096) and both
+    // shapes take the same rows per wave (2 or 4); else the two FCs one after
+    // the other (same results, bit for bit).
+    const int Ca = a.K / 32, Cb = b.K / 32;
+    const int pa = moe_gemv_rows_per_wave(E, a.K, a.N), pb = moe_gemv_rows_per_wave(E, b.K, b.N);
+    if (row_split(Ca).slices != 1 || row_split(Cb).slices != 1 || pa != pb || (pa != 2 && pa != 4)) {
+        hipError_t err = launch_moe_gemv_fp4(a.x, a.x_stride, a.qw, a.s, ids, a.y, E, num_experts, a.K, a.N, stream);
+        if (err != hipSuccess) return err;
+        return launch_moe_gemv_fp4(b.x, b.x_stride, b.qw, b.s, ids, b.y, E, num_experts, b.K, b.N, stream);
+    }
+    const MoeFc f1{static_cast<const u32x4_t*>(a.x), (long)(a.x_stride / 8), reinterpret_cast<const u32x4_t*>(a.qw),
+                   static_cast<const uint16_t*>(a.s), static_cast<uint16_t*>(a.y), Ca, a.N};
+    const MoeFc f2{static_cast<const u32x4_t*>(b.x), (long)(b.x_stride / 8), reinterpret_cast<const u32x4_t*>(b.qw),
+                   static_cast<const uint16_t*>(b.s), static_cast<uint16_t*>(b.y), Cb, b.N};
+    if (pa == 4) return launch_pair_rpt<4>(f1, f2, ids, E, num_experts, stream);
+    return launch_pair_rpt<2>(f1, f2, ids, E, num_experts, stream);
 }
 
 }  // namespace w4

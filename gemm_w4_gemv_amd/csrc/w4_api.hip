@@ -240,6 +240,62 @@ W4_API w4_status w4_moe_gemv(const void* x, int64_t x_stride, const uint8_t* qw_
     return err == hipSuccess ? W4_OK : hip_fail(err, fn);
 }
 
+W4_API w4_status w4_moe_gemv2(const w4_moe_fc* fc1, const w4_moe_fc* fc2, const int32_t* expert_ids, int E,
+                              int num_experts, void* stream) {
+    const char* fn = "w4_moe_gemv2";
+    if (!fc1 || !fc2 || !expert_ids) return fail(W4_ERR_NULL, "%s: fc1, fc2 and expert_ids must not be NULL", fn);
+    if (E < 0) return fail(W4_ERR_SHAPE, "%s: E = %d is negative", fn, E);
+    if (num_experts < 1) return fail(W4_ERR_ARG, "%s: num_experts = %d must be positive", fn, num_experts);
+    if (!aligned(expert_ids, 4)) return fail(W4_ERR_ALIGN, "%s: expert_ids must be 4-byte aligned", fn);
+    const w4_moe_fc* fcs[2] = {fc1, fc2};
+    Range ys[2], ins[2][3];
+    for (int i = 0; i < 2; ++i) {
+        const w4_moe_fc& f = *fcs[i];
+        if (!f.x || !f.qw_fp4 || !f.s_fp4 || !f.y)
+            return fail(W4_ERR_NULL, "%s: fc%d: x, qw_fp4, s_fp4 and y must not be NULL", fn, i + 1);
+        if (f.N < 0) return fail(W4_ERR_SHAPE, "%s: fc%d: N = %d is negative", fn, i + 1, f.N);
+        if (f.K <= 0 || f.K % W4_FP4_GROUP != 0 || f.K > W4_GEMV_MAX_K)
+            return fail(W4_ERR_SHAPE, "%s: fc%d: K = %d must be a positive multiple of 32 up to %d", fn, i + 1, f.K,
+                        W4_GEMV_MAX_K);
+        if ((unsigned long long)f.N * (unsigned long long)(f.K / 2) > W4_GEMV_MAX_MATRIX_BYTES)
+            return fail(W4_ERR_SHAPE, "%s: fc%d: N * K / 2 exceeds %llu bytes", fn, i + 1, W4_GEMV_MAX_MATRIX_BYTES);
+        if (f.x_stride < 0 || f.x_stride % 8 != 0)
+            return fail(W4_ERR_ARG, "%s: fc%d: x_stride = %lld must be a non-negative multiple of 8", fn, i + 1,
+                        (long long)f.x_stride);
+        if (!aligned(f.x, 16) || !aligned(f.qw_fp4, 16))
+            return fail(W4_ERR_ALIGN, "%s: fc%d: x and qw_fp4 must be 16-byte aligned", fn, i + 1);
+        if (!aligned(f.s_fp4, 2) || !aligned(f.y, 2))
+            return fail(W4_ERR_ALIGN, "%s: fc%d: s_fp4 and y must be 2-byte aligned", fn, i + 1);
+        ys[i] = range(f.y, (size_t)E * f.N * 2);
+        const size_t x_elems = E > 0 ? (size_t)(E - 1) * (size_t)f.x_stride + (size_t)f.K : 0;
+        ins[i][0] = range(f.x, x_elems * 2);
+        ins[i][1] = range(f.qw_fp4, (size_t)num_experts * f.N * f.K / 2);
+        ins[i][2] = range(f.s_fp4, (size_t)num_experts * f.N * (f.K / 32) * 2);
+    }
+    const Range rid = range(expert_ids, (size_t)E * 4);
+    for (int i = 0; i < 2; ++i) {
+        if (overlap(ys[i], rid)) return fail(W4_ERR_ALIAS, "%s: fc%d's y overlaps expert_ids", fn, i + 1);
+        for (int j = 0; j < 2; ++j)
+            for (const Range& r : ins[j])
+                if (overlap(ys[i], r))
+                    return fail(W4_ERR_ALIAS, "%s: fc%d's y overlaps an input of fc%d (the two FCs run together)",
+                                fn, i + 1, j + 1);
+    }
+    if (overlap(ys[0], ys[1])) return fail(W4_ERR_ALIAS, "%s: the two outputs overlap", fn);
+    if (E == 0) return W4_OK;
+    if (fc1->N == 0 || fc2->N == 0) {  // one FC only
+        const w4_moe_fc& f = fc1->N == 0 ? *fc2 : *fc1;
+        if (f.N == 0) return W4_OK;
+        hipError_t err = w4::launch_moe_gemv_fp4(f.x, f.x_stride, f.qw_fp4, f.s_fp4, expert_ids, f.y, E, num_experts,
+                                                 f.K, f.N, static_cast<hipStream_t>(stream));
+        return err == hipSuccess ? W4_OK : hip_fail(err, fn);
+    }
+    const w4::MoeFcArgs a{fc1->x, fc1->x_stride, fc1->qw_fp4, fc1->s_fp4, fc1->y, fc1->K, fc1->N};
+    const w4::MoeFcArgs b{fc2->x, fc2->x_stride, fc2->qw_fp4, fc2->s_fp4, fc2->y, fc2->K, fc2->N};
+    hipError_t err = w4::launch_moe_gemv2_fp4(a, b, expert_ids, E, num_experts, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4_OK : hip_fail(err, fn);
+}
+
 W4_API w4_status w4_moe_gemm(const void* x, const int32_t* row_start, const int32_t* expert_ids,
                              const uint8_t* qw_fp4, const void* s_fp4, void* y, int R, int E, int max_rows,
                              int num_experts, int K, int N, void* stream) {

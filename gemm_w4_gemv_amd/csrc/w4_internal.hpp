@@ -40,6 +40,18 @@ hipError_t launch_moe_gemv_fp4(const void* x, int64_t x_stride, const uint8_t* q
                                const void* s, const int32_t* ids, void* y, int E,
                                int num_experts, int K, int N, hipStream_t stream);
 
+// One FC of expert GEMVs, as w4_moe_gemv takes it.
+struct MoeFcArgs {
+    const void* x;
+    int64_t x_stride;
+    const uint8_t* qw;
+    const void* s;
+    void* y;
+    int K, N;
+};
+hipError_t launch_moe_gemv2_fp4(const MoeFcArgs& a, const MoeFcArgs& b, const int32_t* ids, int E, int num_experts,
+                                hipStream_t stream);
+
 hipError_t launch_moe_gemm_fp4(const void* x, const int32_t* row_start, const int32_t* ids, const uint8_t* qw,
                                const void* s, void* y, int R, int E, int max_rows, int num_experts, int K, int N,
                                hipStream_t stream);

@@ -182,6 +182,34 @@ W4_API w4_status w4_moe_gemv(const void* x, int64_t x_stride, const uint8_t* qw_
                              int E, int num_experts, int K, int N, void* stream);
 
 /*
+ * w4_moe_gemv2 -- two FP4 expert FCs over the same E slots and expert ids in
+ * one launch: the result of w4_moe_gemv(fc1) and w4_moe_gemv(fc2), bit for
+ * bit, for two FCs whose inputs are both ready (neither reads the other's
+ * output).  "DeepSeek V4 Triton FP4 优化实战", "深度分析" item 4: every token
+ * runs 2 FC on each of its 6 active experts, all bandwidth-bound, so one
+ * launch saves a launch's ramp and tail.
+ *   w4_moe_fc   { x, x_stride, qw_fp4, s_fp4, y, K, N } -- each field as for
+ *               w4_moe_gemv (fc1 and fc2 each have their own expert pool)
+ *   expert_ids  device int32 [E], 4-byte aligned, for both FCs (read on the
+ *               device; an id outside [0, num_experts) makes that slot's
+ *               outputs of both FCs NaN)
+ * Neither output may overlap any input of either FC, the ids or the other
+ * output.  A FC with N = 0 is skipped.
+ * Errors: as w4_moe_gemv.
+ */
+typedef struct w4_moe_fc {
+    const void* x;        /* device bf16, slot e's vector at x + e * x_stride */
+    int64_t x_stride;     /* elements; 0 shares one vector */
+    const uint8_t* qw_fp4; /* device uint8 [num_experts][N][K/2] */
+    const void* s_fp4;    /* device bf16 [num_experts][N][K/32] */
+    void* y;              /* device bf16 [E][N] */
+    int K;
+    int N;
+} w4_moe_fc;
+W4_API w4_status w4_moe_gemv2(const w4_moe_fc* fc1, const w4_moe_fc* fc2, const int32_t* expert_ids,
+                              int E, int num_experts, void* stream);
+
+/*
  * w4_moe_gemm -- grouped FP4 expert GEMM: several tokens per expert (MoE
  * prefill, or a decode batch routed to experts).
  *   for each group e < E, rows r in [row_start[e], row_start[e+1]):

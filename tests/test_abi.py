@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     for name in names:
         assert hasattr(lib, name), f"libw4.so does not export {name}"
         assert name in w4.SIGNATURES, f"binding has no signature for {name}"
@@ -332,3 +332,25 @@ def test_repack_gptq_validation():
     assert rp(X, S, Z, X + 64, WSP, Y, 256, 64, 128, None) == ALIAS  # qw over qw_kn
     assert rp(X, S, Z, QW, QW + 64, Y, 256, 64, 128, None) == ALIAS  # s over qw
     assert rp(X, S, Z, QW, WSP, Y, 256, 0, 128, None) == OK  # empty: nothing launched
+
+
+def test_moe_gemv2_validation():
+    def fc(x=X, stride=0, qw=QW, s=S, y=Y, K=256, N=64):
+        return w4.MoeFc(x, stride, qw, s, y, K, N)
+    g2 = lib.w4_moe_gemv2
+    ok1, ok2 = fc(), fc(x=X + 0x1000000, qw=QW + 0x1000000, s=S + 0x1000000, y=Y + 0x1000000)
+    assert g2(ctypes.byref(ok1), None, IDS, 6, 64, None) == NULL
+    assert g2(ctypes.byref(ok1), ctypes.byref(ok2), None, 6, 64, None) == NULL
+    bad = fc(K=48)
+    assert g2(ctypes.byref(ok1), ctypes.byref(bad), IDS, 6, 64, None) == SHAPE
+    bad = fc(stride=3)
+    assert g2(ctypes.byref(bad), ctypes.byref(ok2), IDS, 6, 64, None) == ARG
+    bad = fc(qw=QW + 8)
+    assert g2(ctypes.byref(bad), ctypes.byref(ok2), IDS, 6, 64, None) == ALIGN
+    assert g2(ctypes.byref(ok1), ctypes.byref(ok2), IDS, 6, 0, None) == ARG
+    # fc2's output over fc1's input: the two run together
+    bad = fc(x=X + 0x1000000, qw=QW + 0x1000000, s=S + 0x1000000, y=X + 64)
+    assert g2(ctypes.byref(ok1), ctypes.byref(bad), IDS, 6, 64, None) == ALIAS
+    same_y = fc(x=X + 0x1000000, qw=QW + 0x1000000, s=S + 0x1000000, y=Y + 64)
+    assert g2(ctypes.byref(ok1), ctypes.byref(same_y), IDS, 6, 64, None) == ALIAS
+    assert g2(ctypes.byref(ok1), ctypes.byref(ok2), IDS, 0, 64, None) == OK  # empty: nothing launched

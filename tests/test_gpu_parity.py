@@ -380,6 +380,34 @@ def test_moe_full_workload(moe):
                 check_outputs(y[e], y_all[eid, xi], xn[xi], wmax[eid], f"fc{fc + 1} slot {e} expert {eid}")
 
 
+def test_moe_pair_in_one_launch(moe):
+    """w4_moe_gemv2: FC1 (shared x) and FC2 (one x per slot) of the full-size
+    workload in one launch equal the two separate w4_moe_gemv calls bit for
+    bit over 40 tokens' id sets (and so the oracle, checked above), with an
+    out-of-pool id turning that slot of both FCs into NaN."""
+    pools, dev = moe
+    _, x1b, x2b = si.moe_inputs(0)
+    x1, x2 = host.bf16_tensor(x1b), host.bf16_tensor(x2b)
+    (K1, N1), (K2, N2) = si.MOE_FC
+    id_sets = [si.moe_inputs(t)[0] for t in range(40)] + [np.array([3, 64, 7, -1, 0, 63])]
+    for t, ids in enumerate(id_sets):
+        idt = torch.from_numpy(np.asarray(ids, dtype=np.int32)).to(DEV)
+        y1 = torch.full((len(ids), N1), 5.0, dtype=torch.bfloat16, device=DEV)
+        y2 = torch.full((len(ids), N2), 5.0, dtype=torch.bfloat16, device=DEV)
+        w4.w4_moe_gemv2((x1, dev[0]["qw"], dev[0]["s"], y1), (x2, dev[1]["qw"], dev[1]["s"], y2), idt)
+        r1 = torch.empty_like(y1)
+        r2 = torch.empty_like(y2)
+        w4.w4_moe_gemv(x1, dev[0]["qw"], dev[0]["s"], idt, r1)
+        w4.w4_moe_gemv(x2, dev[1]["qw"], dev[1]["s"], idt, r2)
+        torch.cuda.synchronize()
+        for y, r, name in ((y1, r1, "fc1"), (y2, r2, "fc2")):
+            assert same_bits_or_both_nan(y, r), f"token {t} {name}: one launch differs from two"
+        if t == len(id_sets) - 1:
+            bad = torch.tensor([(e < 0 or e >= si.MOE_POOL) for e in ids], device=DEV)
+            for y in (y1, y2):
+                assert torch.all(torch.isnan(y.float()[bad])) and torch.all(torch.isfinite(y.float()[~bad]))
+
+
 def test_moe_invalid_id_gives_nan_and_others_unaffected(moe):
     pools, dev = moe
     _, x1, _ = si.moe_inputs(1)
