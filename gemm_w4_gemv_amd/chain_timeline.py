@@ -4,7 +4,7 @@ A separate build of the library with ``-DW4_CHAIN_TIMELINE`` stamps, per
 workgroup and stage of the last launch, when the stage's staging starts,
 when its x is staged, when its first tile's math starts and when its last
 tile is done (s_memrealtime, 100 MHz).  This script builds that library and,
-on a GPU, runs the decode step of ``bench.py`` (48 layers, 336 INT4 GEMVs
+on a GPU, runs the decode step that ``bench.py`` times (48 layers, 336 INT4 GEMVs
 linked as a decoder reads them, six stages per layer) with it and prints a
 per-stage summary as Markdown.
 
@@ -75,17 +75,14 @@ def run() -> int:
     sys.path.insert(0, str(ROOT))
     import numpy as np
     import torch
-    import seeded_inputs as si
     import gemm_w4_gemv_amd as w4
-    from gemm_w4_gemv_amd import host
-    from gemm_w4_gemv_amd.decode import DecodeStep, LAYER_STAGES
-    import bench
+    from gemm_w4_gemv_amd.decode import DecodeStep, LAYER_STAGES, decode_linears, linked_copy
 
     assert w4.LIB_PATH == TIMELINE_LIB, w4.LIB_PATH
     read = w4.lib.w4_chain_timeline_read
     read.restype = ctypes.c_int
     read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
-    lins = bench.linked_copy(bench.decode_linears(host, si, torch))
+    lins = linked_copy(decode_linears("cuda"))
     step = DecodeStep(lins, mode="chain")
     step.capture()
     for _ in range(5):

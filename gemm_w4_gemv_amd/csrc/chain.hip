@@ -13,17 +13,17 @@
 //
 // The chain is a list of stages.  GEMVs of one stage are independent (q, k, v;
 // gate, up); a GEMV of stage s may read, as its x, the output of a GEMV of an
-// earlier stage.  One 1024-thread workgroup runs per compute unit, its 16
-// waves in two roles:
+// earlier stage.  One 768-thread workgroup runs per compute unit, its 12
+// waves (three per SIMD) in two roles:
 //
 //  * kChainComputeWaves compute waves.  The tiles of each stage are split
 //    evenly over all compute waves of the GPU.  A tile is kChainTileRows
 //    slot-rows of 2 chunks (16 bytes of codes) per lane; x comes from LDS.
-//    A wave keeps two tiles in flight in two register sets used in turn:
-//    while one is computed the next one loads, and the set just computed is
-//    refilled with the tile after next (a dummy load of an empty buffer range
-//    past the wave's last tile, so every step issues the same loads and the
-//    compiler's wait counts stay exact).  A wave publishes, in its own LDS
+//    A wave keeps three tiles in flight in three register sets used in turn:
+//    while one is computed the next two load, and the set just computed is
+//    refilled with the tile three ahead (a dummy load of an empty buffer
+//    range past the wave's last tile, so every step issues the same loads
+//    and the compiler's wait counts stay exact).  A wave publishes, in its own LDS
 //    word, how many stages it has finished; it never waits for its own stores.
 //  * Staging waves (the rest).  Stage t's x vectors go into LDS buffer t & 1
 //    in the dot2 pair layout once every compute wave of the workgroup is past
@@ -344,26 +344,42 @@ __device__ __forceinline__ void stage_load(const ChainLaunch& L, int g, int m, i
     for (int p = 0; p < 4; ++p) raw[p] = buf_load_b128<0>(rx, c * 64u + 16u * p, 0);
 }
 
-// x of chunk m * 64 + lane of GEMV g from its producer's copy in this
-// launch's half: poll (device-coherent loads, bounded) until none of its 32
-// values is the empty mark.  False on time-out.
-__device__ __forceinline__ bool stage_poll(const ChainLaunch& L, Shared& sh, int g, int m, int lane, u32x4_t raw[4]) {
-    const ChainGemv& G = L.gemvs[g];
+// All 32 values of a polled 64-byte chunk are written (none is the empty mark).
+__device__ __forceinline__ bool chunk_filled(const u32x4_t raw[4]) {
+    unsigned ok = 1u;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) ok &= filled(raw[p].x) & filled(raw[p].y) & filled(raw[p].z) & filled(raw[p].w);
+    return ok != 0u;
+}
+
+// x of chunk m * 64 + lane of GEMV g (and, with ``two``, of chunk m1 * 64 +
+// lane of GEMV g1) from the producers' copies in this launch's half: poll
+// both (device-coherent loads, bounded; a lane reloads only what is not yet
+// complete) until none of their values is the empty mark.  False on
+// time-out.
+__device__ __forceinline__ bool stage_poll(const ChainLaunch& L, Shared& sh, int g, int m, bool two, int g1, int m1,
+                                           int lane, u32x4_t raw[4], u32x4_t raw1[4]) {
     const uint32_t off = sh.mirror_off;
-    const __amdgpu_buffer_rsrc_t rm = make_rsrc(G.xm, off + (uint32_t)G.C * 64u);
-    const int c = m * kWave + lane;
-    bool done = c >= G.C;  // padding chunks are staged as zeros
+    const ChainGemv& A = L.gemvs[g];
+    const ChainGemv& B = L.gemvs[g1];
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A.xm, off + (uint32_t)A.C * 64u);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B.xm, off + (uint32_t)B.C * 64u);
+    const int ca = m * kWave + lane, cb = m1 * kWave + lane;
+    bool da = ca >= A.C;  // padding chunks are staged as zeros
+    bool db = !two || cb >= B.C;
     unsigned n = 0;
     for (;;) {
-        if (!done) {
+        if (!da) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) raw[p] = buf_load_b128_coherent(rm, off + (uint32_t)c * 64u + 16u * p, 0);
-            bool ok = true;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) ok &= (filled(raw[p].x) & filled(raw[p].y) & filled(raw[p].z) & filled(raw[p].w)) != 0u;
-            done = ok;
+            for (int p = 0; p < 4; ++p) raw[p] = buf_load_b128_coherent(ra, off + (uint32_t)ca * 64u + 16u * p, 0);
         }
-        if (__builtin_amdgcn_ballot_w64(!done) == 0) break;
+        if (!db) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) raw1[p] = buf_load_b128_coherent(rb, off + (uint32_t)cb * 64u + 16u * p, 0);
+        }
+        if (!da) da = chunk_filled(raw);
+        if (!db) db = chunk_filled(raw1);
+        if (__builtin_amdgcn_ballot_w64(!(da & db)) == 0) break;
         if (lds_load(&sh.abort) || ++n > L.spin_limit) return false;
         // A short pause: a round trip takes about a microsecond, and longer
         // pauses (8) measured 2 % slower on the decode step.
@@ -392,9 +408,9 @@ __device__ __forceinline__ void stage_write(const ChainLaunch& L, int g, int m, 
     *reinterpret_cast<float*>(xg + (size_t)64 * Cp + (size_t)c * 4) = sum;
 }
 
-// This staging wave's share of stage s: slots sid, sid + kChainStagers, ...
-// External inputs two slots at a time; inputs from earlier GEMVs one at a
-// time, polled.  False if a poll timed out.
+// This staging wave's share of stage s: slots sid, sid + kChainStagers, ...,
+// two at a time (inputs from earlier GEMVs polled together).  False if a
+// poll timed out.
 __device__ bool stage_share(const ChainLaunch& L, Shared& sh, int s, unsigned char* xb, int lane, int sid) {
     const ChainStage st = L.stages[s];
     const int n = stage_slots(L, st);
@@ -403,9 +419,11 @@ __device__ bool stage_share(const ChainLaunch& L, Shared& sh, int s, unsigned ch
         stage_slot(L, st, k, g0, m0);
         u32x4_t r0[4], r1[4];
         if (L.gemvs[g0].x_internal) {
-            if (!stage_poll(L, sh, g0, m0, lane, r0)) return false;
+            const bool two = stage_slot(L, st, k + kChainStagers, g1, m1) && L.gemvs[g1].x_internal;
+            if (!stage_poll(L, sh, g0, m0, two, two ? g1 : g0, two ? m1 : m0, lane, r0, r1)) return false;
             stage_write(L, g0, m0, lane, r0, xb);
-            k += kChainStagers;
+            if (two) stage_write(L, g1, m1, lane, r1, xb);
+            k += two ? 2 * kChainStagers : kChainStagers;
             continue;
         }
         const bool two = stage_slot(L, st, k + kChainStagers, g1, m1) && !L.gemvs[g1].x_internal;
@@ -518,27 +536,32 @@ __device__ void compute_wave(const ChainLaunch& L, Shared& sh, const unsigned ch
 
     if (a.s >= L.num_stages) return;
 
-    // Two tiles in flight per wave, in two register sets used in turn: while
-    // one tile is computed the next one loads, and after the math the set is
-    // refilled with the tile after next.  Past the wave's last tile the refill
-    // is a dummy (an empty buffer range, which returns zeros without touching
-    // memory), so every step issues the same loads and the compiler's wait
-    // before a tile's math covers exactly that tile.  No wave ever waits for
-    // its own stores: readers poll the output copies.
-    TileRegs R0, R1;
+    // Three tiles in flight per wave, in three register sets used in turn:
+    // while one tile is computed the next two load, and after the math the set
+    // is refilled with the tile three ahead.  Past the wave's last tile the
+    // refill is a dummy (an empty buffer range, which returns zeros without
+    // touching memory), so every step issues the same loads and the
+    // compiler's wait before a tile's math covers exactly that tile.  No wave
+    // ever waits for its own stores: readers poll the output copies.
+    TileRegs R0, R1, R2;
+    const int S = L.num_stages;
     Work cur = a;
-    Work nxt = advance(L, cur, v, W);
+    Work nx1 = advance(L, cur, v, W);
+    Work nx2 = nx1.s < S ? advance(L, nx1, v, W) : nx1;
     ChainGemv Gc = L.gemvs[cur.g];
-    ChainGemv Gn = L.gemvs[nxt.s < L.num_stages ? nxt.g : cur.g];
+    ChainGemv G1 = L.gemvs[nx1.s < S ? nx1.g : cur.g];
+    ChainGemv G2 = L.gemvs[nx2.s < S ? nx2.g : cur.g];
     issue(Gc, cur, false, lane, R0);
-    issue(Gn, nxt.s < L.num_stages ? nxt : cur, nxt.s >= L.num_stages, lane, R1);
-    // Compute cur from Rc (nxt is loading in the other set); refill Rc with
-    // the tile after nxt.  False once cur was the wave's last tile.
+    issue(G1, nx1.s < S ? nx1 : cur, nx1.s >= S, lane, R1);
+    issue(G2, nx2.s < S ? nx2 : cur, nx2.s >= S, lane, R2);
+    // Compute cur from Rc (the next two tiles are loading in the other sets);
+    // refill Rc with the tile after them.  False once cur was the wave's last
+    // tile.
     auto step = [&](TileRegs& Rc) -> bool {
-        const bool has_n = nxt.s < L.num_stages;
-        const Work n2 = has_n ? advance(L, nxt, v, W) : nxt;
-        const bool has_n2 = n2.s < L.num_stages;
-        const ChainGemv G2 = L.gemvs[has_n2 ? n2.g : cur.g];
+        const bool has_n = nx1.s < S;
+        const Work n3 = nx2.s < S ? advance(L, nx2, v, W) : nx2;
+        const bool has_n3 = n3.s < S;
+        const ChainGemv G3 = L.gemvs[has_n3 ? n3.g : cur.g];
         if (x_stage != cur.s) {
             wait_x(cur.s);
             x_stage = cur.s;
@@ -548,17 +571,19 @@ __device__ void compute_wave(const ChainLaunch& L, Shared& sh, const unsigned ch
                 L.mirror_half_bytes);
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("" ::: "memory");
-        issue(G2, has_n2 ? n2 : cur, !has_n2, lane, Rc);
-        if (nxt.s != cur.s) report(nxt.s);  // cur was this wave's last tile of its stage
-        if (nxt.s != cur.s && lane == 0) timeline_mark(sh, cur.s, 3, false);
+        issue(G3, has_n3 ? n3 : cur, !has_n3, lane, Rc);
+        if (nx1.s != cur.s) report(nx1.s);  // cur was this wave's last tile of its stage
+        if (nx1.s != cur.s && lane == 0) timeline_mark(sh, cur.s, 3, false);
         if (!has_n) return false;
-        cur = nxt;
-        Gc = Gn;
-        nxt = n2;
-        Gn = G2;
+        cur = nx1;
+        Gc = G1;
+        nx1 = nx2;
+        G1 = G2;
+        nx2 = n3;
+        G2 = G3;
         return true;
     };
-    while (step(R0) && step(R1)) {
+    while (step(R0) && step(R1) && step(R2)) {
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }

@@ -43,7 +43,7 @@ struct ChainStage {
     int x_after;     // latest stage whose outputs the stage reads (-1: none)
 };
 
-constexpr int kChainThreads = 1024;  // 16 waves: kChainComputeWaves compute, the rest staging
+constexpr int kChainThreads = 768;  // 12 waves (3 per SIMD): kChainComputeWaves compute, the rest staging
 constexpr int kChainComputeWaves = 8;
 constexpr int kChainStagers = kChainThreads / 64 - kChainComputeWaves;  // staging waves
 constexpr int kChainMaxWorkers = 1024;
