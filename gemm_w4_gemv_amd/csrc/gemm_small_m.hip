@@ -13,16 +13,24 @@
 //     the widest that still launches 240 workgroups) and all M (<= 16) x
 //     rows; its 8 waves split the K groups, each streaming its own groups
 //     with three or four groups of loads in flight and no barrier inside
-//     the K loop.
+//     the K loop.  A wave issues and computes exactly its own groups (a
+//     wave-uniform exit at the end of its range): with about four groups per
+//     wave on a K = 3840 shape, padding the range to whole rounds of the
+//     ring cost as many dummy loads and MFMA steps as real ones.
 //   * Weights: lane (i, b) of a column block loads 16 bytes (words 4b..4b+3
 //     of one group of row i), so a load instruction reads 16 rows x 64
 //     contiguous bytes.  A 4 x 4 transpose across the four 16-lane rows
 //     (v_permlane32_swap, v_permlane16_swap) leaves word 4t + b in register
 //     t: exactly the B operand of k-slice t (k = 32 t + 8 b .. +7).
-//     Activations are loaded 4 rows x 256 bytes per instruction and put in
-//     the matching A layout through a 4 KB LDS tile of the wave's own (an
-//     A-layout load would cover 16 rows x 64 bytes per instruction, measured
-//     15 % slower at M = 16 on the K15360 shape).
+//     Activations are loaded 4 rows x 256 bytes per instruction, one
+//     instruction per 4 rows of x that exist (ceil(M / 4), a template
+//     parameter), and put in the matching A layout through a 4 KB LDS tile of
+//     the wave's own; the tile's rows past them are never written and only
+//     feed output rows past M, which are not stored (an A-layout load would
+//     cover 16 rows x 64 bytes per instruction, measured 15 % slower at
+//     M = 16 on the K15360 shape, and 7-23 % slower at M = 3..16 together
+//     with weights loaded 4 rows x 256 bytes per instruction and re-laid
+//     through LDS).
 //   * Unpacking uses the bf16 bias trick of the GEMV: 0x4300 | q is exactly
 //     128 + q, 7 integer operations per 8 codes, with the activation pairs
 //     permuted to match.  Per group, sum_k (q - z) s x
@@ -67,8 +75,9 @@ struct Slot {
     u32x4_t a[4];
 };
 
-// kCB column blocks of 16 weight rows per workgroup.
-template <int kCB>
+// kCB column blocks of 16 weight rows per workgroup; kMQ = ceil(M / 4)
+// activation load instructions (4 rows each) per group.
+template <int kCB, int kMQ>
 __global__ __launch_bounds__(kThreads) void gemm_int4_small_m_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ s,
     const uint16_t* __restrict__ z, uint16_t* __restrict__ y, int M, int K, int N) {
@@ -109,14 +118,11 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_small_m_kernel(
     char* xw_lds = lds + kSZBytes + wave * (16 * kGroup * 2);
 
     auto issue = [&](int g, Slot<kCB>& S) {
-        const bool live = g < g1;
-        const uint32_t gg = (uint32_t)(live ? g : g0);
-        const __amdgpu_buffer_rsrc_t rw = live ? rq : make_rsrc(qw, 0u);
-        const __amdgpu_buffer_rsrc_t ra = live ? rx : make_rsrc(x, 0u);
+        const uint32_t gg = (uint32_t)g;
 #pragma unroll
-        for (int c = 0; c < kCB; ++c) S.w[c] = buf_load_b128<kAuxNontemporal>(rw, woff[c], gg * 64u);
+        for (int c = 0; c < kCB; ++c) S.w[c] = buf_load_b128<kAuxNontemporal>(rq, woff[c], gg * 64u);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) S.a[t] = buf_load_b128(ra, aoff[t], gg * 256u);
+        for (int t = 0; t < kMQ; ++t) S.a[t] = buf_load_b128(rx, aoff[t], gg * 256u);
     };
 
     // The first groups' loads go out before the scale staging below, so
@@ -124,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_small_m_kernel(
     Slot<kCB> ring[kSlots];
 #pragma unroll
     for (int d = 0; d < kSlots; ++d) {
-        issue(g0 + d, ring[d]);
+        if (g0 + d < g1) issue(g0 + d, ring[d]);
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -173,12 +179,15 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_small_m_kernel(
         for (int d = 0; d < kSlots; ++d) {
             Slot<kCB>& S = ring[d];
             const int gd = g + d;
+            if (gd >= g1) break;  // wave-uniform: the wave's last groups
             // Activation pairs (x_j, x_{j+4}) of each k-slice, matching the
             // biased weight pairs; the same A against ones gives sum_k x.
             // Through this wave's LDS tile (row r, chunk c at c ^ r) into the
             // MFMA layout: lane (i, b) of k-slice t takes chunk 4 t + b of row i.
+            // Rows past 4 kMQ are never written; they only feed output rows
+            // past M, which are not stored.
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
+            for (int t = 0; t < kMQ; ++t) {
                 const int r = (lane >> 4) + 4 * t;
                 *reinterpret_cast<u32x4_t*>(xw_lds + (r * 16 + (li ^ r)) * 16) = S.a[t];
             }
@@ -194,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_small_m_kernel(
             f32x4_t sx = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int t = 0; t < 4; ++t) sx = mfma(a[t], ones, sx);
-            const int gi = min(gd, g1 - 1);  // a surplus step past the range has zero activations
+            const int gi = gd;
 #pragma unroll
             for (int c = 0; c < kCB; ++c) {
                 u32x4_t w = S.w[c];
@@ -213,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_small_m_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[c][e] = __builtin_fmaf(sc, p[e], __builtin_fmaf(-szb, sx[e], acc[c][e]));
             }
-            issue(gd + kSlots, S);
+            if (gd + kSlots < g1) issue(gd + kSlots, S);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -253,11 +262,20 @@ hipError_t launch_gemm_int4_small_m(const void* x, const int32_t* qw, const void
     uint16_t* yb = static_cast<uint16_t*>(y);
     // Weight rows per workgroup (16 per block) from the per-shape table, else
     // the widest tile that still gives 240 workgroups (the rule in tune.hip).
-    auto launch = [&](auto cb) {
+    auto launch_q = [&](auto cb, auto mq) {
         constexpr int kCB = decltype(cb)::value;
+        constexpr int kMQ = decltype(mq)::value;
         const dim3 grid((unsigned)((N + 16 * kCB - 1) / (16 * kCB)));
-        gemm_int4_small_m_kernel<kCB><<<grid, kThreads, 0, stream>>>(xb, wb, sb, zb, yb, M, K, N);
+        gemm_int4_small_m_kernel<kCB, kMQ><<<grid, kThreads, 0, stream>>>(xb, wb, sb, zb, yb, M, K, N);
         return hipGetLastError();
+    };
+    auto launch = [&](auto cb) {
+        switch ((M + 3) / 4) {
+            case 1: return launch_q(cb, std::integral_constant<int, 1>{});
+            case 2: return launch_q(cb, std::integral_constant<int, 2>{});
+            case 3: return launch_q(cb, std::integral_constant<int, 3>{});
+            default: return launch_q(cb, std::integral_constant<int, 4>{});
+        }
     };
     switch (gemm_small_m_blocks(M, K, N)) {
         case 4: return launch(std::integral_constant<int, 4>{});
