@@ -8,11 +8,13 @@
 // x and applies expert ids[e] to them.
 //
 // gfx950 design (the structure of the small-M INT4 path):
-//   * Grid: (weight-row tiles of 64, 32 or 16 rows) x (slabs of 16 rows of a
+//   * Grid: (weight-row tiles of 32 or 16 rows) x (slabs of 16 rows of a
 //     group) x (groups).  A workgroup whose slab starts past its group's last
 //     row exits at once; an expert id outside the pool turns the slab's
 //     outputs into NaN without reading any weight.
-//   * 8 waves split the K range in steps of 128 k.  Per step, lane (i, b) of
+//   * 8 waves split the K range in steps of 128 k; a wave issues and
+//     computes exactly its own steps (a wave-uniform exit at the end of its
+//     range).  Per step, lane (i, b) of
 //     a column block loads 16 bytes (words 4b..4b+3, 8 codes per word) of
 //     weight row i; a 4 x 4 transpose across the four 16-lane rows
 //     (v_permlane32_swap, v_permlane16_swap) leaves word 4t + b in register
@@ -102,7 +104,6 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp4_kernel(
     const uint16_t* se = s + (size_t)expert * N * G;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qe, (uint32_t)N * row_bytes);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)((size_t)R * K * 2));
-    const __amdgpu_buffer_rsrc_t rnone = make_rsrc(qw, 0u);
 
     // Weights: row n0 + 16 c + i (rows past N read row N - 1, never stored),
     // bytes 16 b .. +15 of the step.  Activations: rows m0 + lane / 16 + 4 i
@@ -116,19 +117,21 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp4_kernel(
     char* xw_lds = lds + kSBytes + wave * (16 * kStep * 2);
 
     auto issue = [&](int g, Slot<kCB>& T) {
-        const bool live = g < g1;
-        const uint32_t gg = (uint32_t)(live ? g : g0);
+        const uint32_t gg = (uint32_t)g;
 #pragma unroll
-        for (int c = 0; c < kCB; ++c) T.w[c] = buf_load_b128<kAuxNontemporal>(live ? rq : rnone, woff[c], gg * 64u);
+        for (int c = 0; c < kCB; ++c) T.w[c] = buf_load_b128<kAuxNontemporal>(rq, woff[c], gg * 64u);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) T.a[t] = buf_load_b128(live ? rx : rnone, aoff[t], gg * 256u);
+        for (int t = 0; t < 4; ++t) T.a[t] = buf_load_b128(rx, aoff[t], gg * 256u);
     };
 
-    constexpr int kSlots = kCB == 4 ? 3 : 4;  // steps of loads in flight per wave (register budget)
+    // Steps of loads in flight per wave: two at 32 rows per workgroup keeps
+    // the kernel within 128 VGPRs, so two workgroups (four waves per SIMD)
+    // share a compute unit.
+    constexpr int kSlots = kCB == 2 ? 2 : 4;
     Slot<kCB> ring[kSlots];
 #pragma unroll
     for (int d = 0; d < kSlots; ++d) {
-        issue(g0 + d, ring[d]);
+        if (g0 + d < g1) issue(g0 + d, ring[d]);
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -167,6 +170,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp4_kernel(
         for (int d = 0; d < kSlots; ++d) {
             Slot<kCB>& T = ring[d];
             const int gd = g + d;
+            if (gd >= g1) break;  // wave-uniform: the wave's last steps
             // Activations through this wave's LDS tile (row r, chunk c at
             // c ^ r) into the A layout: lane (i, b) of k-slice t takes chunk
             // 4 t + b of row i.
@@ -178,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp4_kernel(
             u32x4_t a[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const u32x4_t*>(xw_lds + (li * 16 + ((4 * t + lb) ^ li)) * 16);
-            const int gi = min(gd, g1 - 1);  // a surplus step past the range has zero activations
+            const int gi = gd;
 #pragma unroll
             for (int c = 0; c < kCB; ++c) {
                 u32x4_t w = T.w[c];
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp4_kernel(
                     for (int e = 0; e < 4; ++e) acc[c][e] = __builtin_fmaf(sc, p[e], acc[c][e]);
                 }
             }
-            issue(gd + kSlots, T);
+            if (gd + kSlots < g1) issue(gd + kSlots, T);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -233,8 +237,10 @@ hipError_t launch_moe_gemm_fp4(const void* x, const int32_t* row_start, const in
     const uint16_t* sb = static_cast<const uint16_t*>(s);
     uint16_t* yb = static_cast<uint16_t*>(y);
     const unsigned slabs = (unsigned)((max_rows + 15) / 16);
-    // The widest tile (64, 32 or 16 weight rows) that still gives at least
-    // 240 workgroups when every group has max_rows rows.
+    // 32 weight rows per workgroup (two workgroups per compute unit) when
+    // that gives at least 240 workgroups for groups of max_rows rows, else
+    // 16.  Measured on 6 experts x 16 rows, FC1 and FC2: 26.1 us per pair
+    // at 32 rows, 29.3 at 16, 30.4 at 64 (one workgroup per compute unit).
     auto launch = [&](auto cb) {
         constexpr int kCB = decltype(cb)::value;
         const dim3 grid((unsigned)((N + 16 * kCB - 1) / (16 * kCB)), slabs, (unsigned)E);
@@ -242,7 +248,6 @@ hipError_t launch_moe_gemm_fp4(const void* x, const int32_t* row_start, const in
         return hipGetLastError();
     };
     const long per = (long)slabs * E;
-    if ((long)((N + 63) / 64) * per >= 240) return launch(std::integral_constant<int, 4>{});
     if ((long)((N + 31) / 32) * per >= 240) return launch(std::integral_constant<int, 2>{});
     return launch(std::integral_constant<int, 1>{});
 }
