@@ -257,15 +257,26 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_mfma_kernel(
     }
 }
 
-// y = bf16(sum over splits of the FP32 partials), splits added in order.
+// y = bf16(sum over splits of the FP32 partials), splits added in order;
+// four consecutive outputs per thread (16-byte partial loads, one 8-byte
+// store), the last few one at a time when M * N is not a multiple of four.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws,
                                                             uint16_t* __restrict__ y, size_t count,
                                                             int splits) {
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t i = 4 * ((size_t)blockIdx.x * blockDim.x + threadIdx.x);
     if (i >= count) return;
-    float t = ws[i];
-    for (int k = 1; k < splits; ++k) t += ws[(size_t)k * count + i];
-    y[i] = f32_to_bf16(t);
+    // (The workspace is 16-byte aligned; y only 2-byte aligned in general.)
+    if (i + 4 <= count && (count & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0) {
+        f32x4_t t = *reinterpret_cast<const f32x4_t*>(ws + i);
+        for (int k = 1; k < splits; ++k) t += *reinterpret_cast<const f32x4_t*>(ws + (size_t)k * count + i);
+        *reinterpret_cast<u32x2_t*>(y + i) = u32x2_t{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])};
+        return;
+    }
+    for (size_t e = i; e < i + 4 && e < count; ++e) {
+        float t = ws[e];
+        for (int k = 1; k < splits; ++k) t += ws[(size_t)k * count + e];
+        y[e] = f32_to_bf16(t);
+    }
 }
 
 
@@ -302,7 +313,7 @@ hipError_t launch_gemm_int4(const void* x, const int32_t* qw, const void* s, con
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const size_t count = (size_t)M * N;
-    const unsigned blocks = (unsigned)((count + 255) / 256);
+    const unsigned blocks = (unsigned)((count + 1023) / 1024);
     splitk_reduce_kernel<<<blocks, 256, 0, stream>>>(ws, yb, count, splits);
     return hipGetLastError();
 }
