@@ -144,7 +144,8 @@ def floors(w4, torch, stream):
     log(f"read probe: {read_gbps:.0f} GB/s over 2 GiB; 336 empty launches: {empty_ms * 1e3:.1f} us per replay")
     return src, sink, {"hbm_read_probe": {"GBps": round(read_gbps, 1), "frac_hbm": round(read_gbps / 8000.0, 4),
                                           "bytes": src.numel(),
-                                          "note": "plain streaming read kernel of this library (w4_read_probe); "
+                                          "note": "plain streaming read kernel of this library (w4_read_probe: "
+                                                  "512 workgroups, each streaming one contiguous 4 MiB region); "
                                                   "median of 5 trials of 5 launches"},
                        "empty_336_launch_graph_us": round(empty_ms * 1e3, 1)}
 
