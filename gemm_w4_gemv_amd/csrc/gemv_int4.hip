@@ -32,16 +32,38 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// All loads are issued before any of their results is used, from offsets clamped into the arrays, so a wave keeps RPT x CPL weight
-// loads in flight without branches.  Clamped duplicates are harmless: a
-// chunk past the row end gets x = 0 (contributes nothing) and a row past N
-// is never stored.  Weights, scales and zeros are read with buffer loads:
-// the row offset is wave-uniform (SGPR), the lane offset 32-bit.
+// All loads are issued before any of their results is used, from offsets
+// clamped into the arrays, so a wave keeps RPT x CPL weight loads in flight
+// without branches.  Clamped duplicates are harmless: a chunk past the row
+// end gets x = 0 (contributes nothing) and a row past N is never stored.
+// Weights are read with buffer loads: the row offset is wave-uniform (SGPR),
+// the lane offset 32-bit.
+//
+// x is staged once per workgroup in LDS (each workgroup's waves share it):
+// thread t loads 16-byte pieces t, t + 256, ... of x (coalesced, issued
+// before the weights), piece p of chunk c lands at p * kXChunks + c, and
+// chunks past the row end are zeros.  Each row's scales and zeros come from
+// one load per row (two past 32 groups per K-slice): lane l < 32 loads the
+// scale of the slice's group l, lane l >= 32 the zero of group l - 32, and a
+// lane gathers its chunk's pair with ds_bpermute.  Loading x per wave and
+// two 2-byte values per chunk and row instead read 8 KB of x per wave from
+// L2 and issued four scale/zero load instructions per row: each cost 13-15 %
+// of the logits GEMV's time.
 template <int S, int CPL, int RPT>
 __global__ __launch_bounds__(kThreads) void gemv_int4_kernel(
     const u32x4_t* __restrict__ qw, const uint16_t* __restrict__ s, const uint16_t* __restrict__ z,
     const u32x4_t* __restrict__ x, uint16_t* __restrict__ y, int C, int N) {
-    constexpr int T = 4 / S;  // row teams per workgroup
+    constexpr int T = 4 / S;                    // row teams per workgroup
+    constexpr int kXChunks = S * CPL * kWave;   // staged chunks (the row, padded)
+    constexpr int kPerThread = kXChunks * 4 / kThreads;  // 16-byte pieces each thread stages
+    constexpr int kSliceGroups = CPL * kWave / 4;
+    constexpr bool kOneSZ = kSliceGroups <= 32;  // scale and zero of a row in one load
+    // Staging pays when several row teams share x; with one team (a row cut
+    // over all four waves) each wave loads its own slice straight into
+    // registers.
+    constexpr bool kStageX = T >= 2;
+    static_assert(kXChunks * 4 % kThreads == 0, "whole pieces per thread");
+    __shared__ u32x4_t xs[kStageX ? 4 * kXChunks : 1];
     __shared__ float part[S][T * RPT];
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -51,28 +73,50 @@ __global__ __launch_bounds__(kThreads) void gemv_int4_kernel(
     const int G = C >> 2;  // groups of 128 per row
     const uint32_t row_bytes = (uint32_t)C * 16u;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(qw, (uint32_t)N * row_bytes);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, row_bytes * 4u);  // C chunks of 64 bytes; past them reads 0
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, (uint32_t)N * (uint32_t)G * 2u);
     const __amdgpu_buffer_rsrc_t rz = make_rsrc(z, (uint32_t)N * (uint32_t)G * 2u);
 
-    int c[CPL];
-    bool ok[CPL];
+    // x first: its loads complete before the weights', which are issued after it.
+    u32x4_t xload[kStageX ? kPerThread : 4 * CPL];
+    if constexpr (kStageX) {
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const int ci = slice * kWave * CPL + i * kWave + lane;
-        ok[i] = ci < C;
-        c[i] = ok[i] ? ci : C - 1;
+        for (int j = 0; j < kPerThread; ++j)
+            xload[j] = buf_load_b128(rx, (uint32_t)(threadIdx.x + kThreads * j) * 16u, 0u);
+    } else {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                xload[4 * i + p] = buf_load_b128(rx, (uint32_t)(slice * kWave * CPL + i * kWave + lane) * 64u + 16u * p, 0u);
     }
 
-    // x first (small, cache-resident): its pairs are built while the weights stream in.
-    u32x4_t xraw[CPL][4];
+    int c[CPL];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) xraw[i][p] = x[4 * c[i] + p];
+    for (int i = 0; i < CPL; ++i) c[i] = min(slice * kWave * CPL + i * kWave + lane, C - 1);
 
     const int row0 = (blockIdx.x * T + team) * RPT;
     u32x4_t wv[RPT][CPL];
-    uint16_t sraw[RPT][CPL], zraw[RPT][CPL];
+    uint32_t sz0[RPT], sz1[RPT];
+    // Scales and zeros before the weights: the rows' math waits for them,
+    // and loads complete in issue order, so row r's math can start as soon
+    // as row r's weights are in.
+    const int g0 = slice * kSliceGroups;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const uint32_t roff = (uint32_t)min(row0 + r, N - 1) * (uint32_t)G * 2u;
+        if constexpr (kOneSZ) {
+            const uint32_t goff = (uint32_t)min(g0 + (lane & 31), G - 1) * 2u;
+            // Lanes 0-31 read the scale, 32-63 the zero: two buffers, each lane
+            // in range for one of them only (the other read returns 0).
+            sz0[r] = (uint32_t)buf_load_u16(rs, lane < 32 ? goff : 0x80000000u, roff) |
+                     (uint32_t)buf_load_u16(rz, lane < 32 ? 0x80000000u : goff, roff);
+        } else {
+            const uint32_t goff = (uint32_t)min(g0 + lane, G - 1) * 2u;
+            sz0[r] = buf_load_u16(rs, goff, roff);
+            sz1[r] = buf_load_u16(rz, goff, roff);
+        }
+    }
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
         const uint32_t row = (uint32_t)min(row0 + r, N - 1);
@@ -80,28 +124,26 @@ __global__ __launch_bounds__(kThreads) void gemv_int4_kernel(
         for (int i = 0; i < CPL; ++i)
             wv[r][i] = buf_load_b128<kAuxNontemporal>(rw, (uint32_t)c[i] * 16u, row * row_bytes);
     }
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-        const uint32_t row = (uint32_t)min(row0 + r, N - 1);
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const uint32_t goff = (uint32_t)(c[i] >> 2) * 2u;
-            sraw[r][i] = buf_load_u16(rs, goff, row * (uint32_t)G * 2u);
-            zraw[r][i] = buf_load_u16(rz, goff, row * (uint32_t)G * 2u);
-        }
-    }
     __builtin_amdgcn_sched_barrier(0);  // keep every load above ahead of the math below
+
+    if constexpr (kStageX) {
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            const int q = threadIdx.x + kThreads * j;  // piece p = q % 4 of chunk q / 4
+            xs[(q & 3) * kXChunks + (q >> 2)] = xload[j];
+        }
+        __syncthreads();
+    }
 
     uint32_t xp[CPL][16];
     float sx[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-        sx[i] = x_chunk_pairs(xraw[i], xp[i]);
-        if (!ok[i]) {
-            sx[i] = 0.f;
+        u32x4_t xraw[4];
+        const int cx = slice * kWave * CPL + i * kWave + lane;  // chunks past C read zeros
 #pragma unroll
-            for (int j = 0; j < 16; ++j) xp[i][j] = 0u;
-        }
+        for (int p = 0; p < 4; ++p) xraw[p] = kStageX ? xs[p * kXChunks + cx] : xload[4 * i + p];
+        sx[i] = x_chunk_pairs(xraw, xp[i]);
     }
 
     const uint32_t bias = vgpr_const(kInt4BiasPair);
@@ -111,9 +153,18 @@ __global__ __launch_bounds__(kThreads) void gemv_int4_kernel(
         acc[r] = 0.f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
+            const int gi = 16 * i + (lane >> 2);  // the chunk's group within the slice
+            uint32_t sb, zbits;
+            if constexpr (kOneSZ) {
+                sb = (uint32_t)__shfl((int)sz0[r], gi, kWave);
+                zbits = (uint32_t)__shfl((int)sz0[r], 32 + gi, kWave);
+            } else {
+                sb = (uint32_t)__shfl((int)sz0[r], gi, kWave);
+                zbits = (uint32_t)__shfl((int)sz1[r], gi, kWave);
+            }
             const float d = chunk_dot(wv[r][i], xp[i], bias);
-            const float zb = f16_to_f32(zraw[r][i]) + 128.f;
-            acc[r] = __builtin_fmaf(f16_to_f32(sraw[r][i]), __builtin_fmaf(-zb, sx[i], d), acc[r]);
+            const float zb = f16_to_f32((uint16_t)zbits) + 128.f;
+            acc[r] = __builtin_fmaf(f16_to_f32((uint16_t)sb), __builtin_fmaf(-zb, sx[i], d), acc[r]);
         }
     }
 
