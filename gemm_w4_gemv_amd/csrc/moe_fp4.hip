@@ -52,16 +52,43 @@ struct MoeFc {
 };
 
 // Rows [bx T RPT, (bx + 1) T RPT) of slot ``slot``: the work of one workgroup.
+// x is loaded before the expert id is known (it depends on the slot only);
+// when several row teams share it, it is staged once per workgroup in LDS
+// (thread t loads 16-byte pieces t, t + 256, ...; piece p of chunk c lands
+// at p * S * CPL * 64 + c, chunks past the row end read zeros), else each
+// wave loads its own slice.
 template <int S, int CPL, int RPT>
 __device__ __forceinline__ void moe_gemv_rows(const MoeFc& f, const int32_t* __restrict__ ids, int num_experts,
-                                              int bx, int slot, float (&part)[S][(4 / S) * RPT]) {
+                                              int bx, int slot, float (&part)[S][(4 / S) * RPT], u32x4_t* xs) {
     constexpr int T = 4 / S;
-    const u32x4_t* __restrict__ x = f.x;
+    constexpr bool kStageX = T >= 2;
+    constexpr int kXChunks = S * CPL * kWave;
+    constexpr int kPerThread = kXChunks * 4 / kThreads;
+    static_assert(kXChunks * 4 % kThreads == 0, "whole pieces per thread");
     const u32x4_t* __restrict__ qw = f.qw;
     const uint16_t* __restrict__ s = f.s;
     uint16_t* __restrict__ y = f.y;
-    const long x_stride_vec = f.x_stride_vec;
     const int C = f.C, N = f.N;
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int slice = wave % S;
+    const int team = wave / S;
+    const uint32_t row_bytes = (uint32_t)C * 16u;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(f.x + (size_t)slot * f.x_stride_vec, row_bytes * 4u);
+
+    u32x4_t xload[kStageX ? kPerThread : 4 * CPL];
+    if constexpr (kStageX) {
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j)
+            xload[j] = buf_load_b128(rx, (uint32_t)(threadIdx.x + kThreads * j) * 16u, 0u);
+    } else {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                xload[4 * i + p] = buf_load_b128(rx, (uint32_t)(slice * kWave * CPL + i * kWave + lane) * 64u + 16u * p, 0u);
+    }
 
     const int expert = ids[slot];
     if (expert < 0 || expert >= num_experts) {  // uniform across the workgroup
@@ -71,29 +98,16 @@ __device__ __forceinline__ void moe_gemv_rows(const MoeFc& f, const int32_t* __r
         }
         return;
     }
-
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int slice = wave % S;
-    const int team = wave / S;
-    const u32x4_t* xs = x + (size_t)slot * x_stride_vec;
-    const uint32_t row_bytes = (uint32_t)C * 16u;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(qw + (size_t)expert * N * C, (uint32_t)N * row_bytes);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(s + (size_t)expert * N * C, (uint32_t)N * (uint32_t)C * 2u);
 
-    // Clamped, branch-free loads (see the INT4 GEMV): x, then weights, then scales.
+    // Clamped, branch-free loads (see the INT4 GEMV): scales, then weights.
     int c[CPL];
-    bool ok[CPL];
-    u32x4_t xraw[CPL][4];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const int ci = slice * kWave * CPL + i * kWave + lane;
-        ok[i] = ci < C;
-        c[i] = ok[i] ? ci : C - 1;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) xraw[i][p] = xs[4 * c[i] + p];
-    }
+    for (int i = 0; i < CPL; ++i) c[i] = min(slice * kWave * CPL + i * kWave + lane, C - 1);
 
+    // Scales before the weights: loads complete in issue order, so row r's
+    // math can start as soon as row r's weights are in.
     const int row0 = (bx * T + team) * RPT;
     u32x4_t wv[RPT][CPL];
     uint16_t sraw[RPT][CPL];
@@ -101,26 +115,36 @@ __device__ __forceinline__ void moe_gemv_rows(const MoeFc& f, const int32_t* __r
     for (int r = 0; r < RPT; ++r) {
         const uint32_t row = (uint32_t)min(row0 + r, N - 1);
 #pragma unroll
-        for (int i = 0; i < CPL; ++i)
-            wv[r][i] = buf_load_b128<kAuxNontemporal>(rw, (uint32_t)c[i] * 16u, row * row_bytes);
+        for (int i = 0; i < CPL; ++i) sraw[r][i] = buf_load_u16(rs, (uint32_t)c[i] * 2u, row * (uint32_t)C * 2u);
     }
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
         const uint32_t row = (uint32_t)min(row0 + r, N - 1);
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) sraw[r][i] = buf_load_u16(rs, (uint32_t)c[i] * 2u, row * (uint32_t)C * 2u);
+        for (int i = 0; i < CPL; ++i)
+            wv[r][i] = buf_load_b128<kAuxNontemporal>(rw, (uint32_t)c[i] * 16u, row * row_bytes);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep every load above ahead of the math below
 
+    if constexpr (kStageX) {
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            const int q = threadIdx.x + kThreads * j;  // piece p = q % 4 of chunk q / 4
+            xs[(q & 3) * kXChunks + (q >> 2)] = xload[j];
+        }
+        __syncthreads();
+    }
     uint32_t xp[CPL][16];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
+        const int cx = slice * kWave * CPL + i * kWave + lane;  // chunks past C read zeros
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            xp[i][4 * p + 0] = ok[i] ? xraw[i][p].x : 0u;
-            xp[i][4 * p + 1] = ok[i] ? xraw[i][p].y : 0u;
-            xp[i][4 * p + 2] = ok[i] ? xraw[i][p].z : 0u;
-            xp[i][4 * p + 3] = ok[i] ? xraw[i][p].w : 0u;
+            const u32x4_t v = kStageX ? xs[p * kXChunks + cx] : xload[4 * i + p];
+            xp[i][4 * p + 0] = v.x;
+            xp[i][4 * p + 1] = v.y;
+            xp[i][4 * p + 2] = v.z;
+            xp[i][4 * p + 3] = v.w;
         }
     }
     float sv[RPT][CPL];
@@ -154,7 +178,8 @@ template <int S, int CPL, int RPT>
 __global__ __launch_bounds__(kThreads) void moe_gemv_fp4_kernel(MoeFc f, const int32_t* __restrict__ ids,
                                                                 int num_experts) {
     __shared__ float part[S][(4 / S) * RPT];
-    moe_gemv_rows<S, CPL, RPT>(f, ids, num_experts, blockIdx.x, blockIdx.y, part);
+    __shared__ u32x4_t xs[(4 / S) >= 2 ? 4 * S * CPL * kWave : 1];
+    moe_gemv_rows<S, CPL, RPT>(f, ids, num_experts, blockIdx.x, blockIdx.y, part, xs);
 }
 
 // Two FCs over the same slots and expert ids in one launch: workgroups
@@ -166,8 +191,9 @@ __global__ __launch_bounds__(kThreads) void moe_gemv2_fp4_kernel(MoeFc f1, MoeFc
                                                                  const int32_t* __restrict__ ids,
                                                                  int num_experts) {
     __shared__ float part[1][4 * RPT];
-    if ((int)blockIdx.x < b1) moe_gemv_rows<1, CPL1, RPT>(f1, ids, num_experts, blockIdx.x, blockIdx.y, part);
-    else moe_gemv_rows<1, CPL2, RPT>(f2, ids, num_experts, blockIdx.x - b1, blockIdx.y, part);
+    __shared__ u32x4_t xs[4 * (CPL1 > CPL2 ? CPL1 : CPL2) * kWave];
+    if ((int)blockIdx.x < b1) moe_gemv_rows<1, CPL1, RPT>(f1, ids, num_experts, blockIdx.x, blockIdx.y, part, xs);
+    else moe_gemv_rows<1, CPL2, RPT>(f2, ids, num_experts, blockIdx.x - b1, blockIdx.y, part, xs);
 }
 
 template <int S, int CPL, int RPT>
