@@ -65,7 +65,15 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_int4_kernel(
     const u32x4_t* __restrict__ x, uint16_t* __restrict__ y, int M, int C, int N) {
     constexpr int T = 4 / S;      // row teams per workgroup
     constexpr int R = RPT * MX;   // sums per wave: (weight row, x row)
+    // x staged once per workgroup in LDS when row teams share it (piece p of
+    // chunk c of x row m at (m * 4 + p) * kXChunks + c, chunks past the row
+    // end zeros), else loaded per wave.
+    constexpr bool kStageX = T >= 2;
+    constexpr int kXChunks = S * CPL * kWave;
+    constexpr int kPerThread = MX * kXChunks * 4 / kThreads;
+    static_assert(kXChunks * 4 % kThreads == 0, "whole pieces per thread");
     __shared__ float part[S][T * R];
+    __shared__ u32x4_t xs[kStageX ? MX * 4 * kXChunks : 1];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -78,35 +86,38 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_int4_kernel(
     const __amdgpu_buffer_rsrc_t rz = make_rsrc(z, (uint32_t)N * (uint32_t)G * 2u);
 
     int c[CPL];
-    bool ok[CPL];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const int ci = slice * kWave * CPL + i * kWave + lane;
-        ok[i] = ci < C;
-        c[i] = ok[i] ? ci : C - 1;
+    for (int i = 0; i < CPL; ++i) c[i] = min(slice * kWave * CPL + i * kWave + lane, C - 1);
+
+    // x first (small, cache-resident); a row of x is C chunks of 4 x 16 bytes
+    // (reads past it return zeros).
+    u32x4_t xload[kStageX ? kPerThread : MX * CPL * 4];
+    if constexpr (kStageX) {
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            const int q = threadIdx.x + kThreads * j;  // piece of x row q / (4 kXChunks)
+            const int m = q / (4 * kXChunks), qq = q % (4 * kXChunks);
+            const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (size_t)min(m, M - 1) * (size_t)C * 4u, row_bytes * 4u);
+            xload[j] = buf_load_b128(rx, (uint32_t)qq * 16u, 0u);
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < MX; ++m) {
+            const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (size_t)min(m, M - 1) * (size_t)C * 4u, row_bytes * 4u);
+#pragma unroll
+            for (int i = 0; i < CPL; ++i)
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    xload[(m * CPL + i) * 4 + p] =
+                        buf_load_b128(rx, (uint32_t)(slice * kWave * CPL + i * kWave + lane) * 64u + 16u * p, 0u);
+        }
     }
 
-    // x first (small, cache-resident); a row of x is C chunks of 4 x 16 bytes.
-    u32x4_t xraw[MX][CPL][4];
-#pragma unroll
-    for (int m = 0; m < MX; ++m) {
-        const u32x4_t* xm = x + (size_t)min(m, M - 1) * (size_t)C * 4u;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i)
-#pragma unroll
-            for (int p = 0; p < 4; ++p) xraw[m][i][p] = xm[4 * c[i] + p];
-    }
-
+    // Scales and zeros before the weights: loads complete in issue order, so
+    // row r's math can start as soon as row r's weights are in.
     const int row0 = (blockIdx.x * T + team) * RPT;
     u32x4_t wv[RPT][CPL];
     uint16_t sraw[RPT][CPL], zraw[RPT][CPL];
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-        const uint32_t row = (uint32_t)min(row0 + r, N - 1);
-#pragma unroll
-        for (int i = 0; i < CPL; ++i)
-            wv[r][i] = buf_load_b128<kAuxNontemporal>(rw, (uint32_t)c[i] * 16u, row * row_bytes);
-    }
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
         const uint32_t row = (uint32_t)min(row0 + r, N - 1);
@@ -117,7 +128,24 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_int4_kernel(
             zraw[r][i] = buf_load_u16(rz, goff, row * (uint32_t)G * 2u);
         }
     }
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const uint32_t row = (uint32_t)min(row0 + r, N - 1);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            wv[r][i] = buf_load_b128<kAuxNontemporal>(rw, (uint32_t)c[i] * 16u, row * row_bytes);
+    }
     __builtin_amdgcn_sched_barrier(0);  // keep every load above ahead of the math below
+
+    if constexpr (kStageX) {
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            const int q = threadIdx.x + kThreads * j;
+            const int m = q / (4 * kXChunks), qq = q % (4 * kXChunks);  // piece qq % 4 of chunk qq / 4
+            xs[(m * 4 + (qq & 3)) * kXChunks + (qq >> 2)] = xload[j];
+        }
+        __syncthreads();
+    }
 
     uint32_t xp[CPL][MX][16];
     float sx[CPL][MX];
@@ -125,12 +153,11 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_int4_kernel(
     for (int i = 0; i < CPL; ++i)
 #pragma unroll
         for (int m = 0; m < MX; ++m) {
-            sx[i][m] = x_chunk_pairs(xraw[m][i], xp[i][m]);
-            if (!ok[i]) {
-                sx[i][m] = 0.f;
+            const int cx = slice * kWave * CPL + i * kWave + lane;  // chunks past C read zeros
+            u32x4_t xraw[4];
 #pragma unroll
-                for (int j = 0; j < 16; ++j) xp[i][m][j] = 0u;
-            }
+            for (int p = 0; p < 4; ++p) xraw[p] = kStageX ? xs[(m * 4 + p) * kXChunks + cx] : xload[(m * CPL + i) * 4 + p];
+            sx[i][m] = x_chunk_pairs(xraw, xp[i][m]);
         }
 
     const uint32_t bias = vgpr_const(kInt4BiasPair);
