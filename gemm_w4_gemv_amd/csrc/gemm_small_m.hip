@@ -180,26 +180,25 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_small_m_kernel(
             Slot<kCB>& S = ring[d];
             const int gd = g + d;
             if (gd >= g1) break;  // wave-uniform: the wave's last groups
-            // Activation pairs (x_j, x_{j+4}) of each k-slice, matching the
-            // biased weight pairs; the same A against ones gives sum_k x.
-            // Through this wave's LDS tile (row r, chunk c at c ^ r) into the
-            // MFMA layout: lane (i, b) of k-slice t takes chunk 4 t + b of row i.
-            // Rows past 4 kMQ are never written; they only feed output rows
-            // past M, which are not stored.
+            // Activation pairs (x_j, x_{j+4}) of each 16-byte chunk, matching
+            // the biased weight pairs, built as the chunk goes into this wave's
+            // LDS tile (row r, chunk c at c ^ r: each lane converts ceil(M / 4)
+            // chunks, not the four it reads back); read in the MFMA layout:
+            // lane (i, b) of k-slice t takes chunk 4 t + b of row i.  The same
+            // A against ones gives sum_k x.  Rows past 4 kMQ are never
+            // written; they only feed output rows past M, which are not stored.
 #pragma unroll
             for (int t = 0; t < kMQ; ++t) {
                 const int r = (lane >> 4) + 4 * t;
-                *reinterpret_cast<u32x4_t*>(xw_lds + (r * 16 + (li ^ r)) * 16) = S.a[t];
+                const uint32_t xw[4] = {S.a[t].x, S.a[t].y, S.a[t].z, S.a[t].w};
+                uint32_t p[4];
+                x_pairs_for_biased(xw, p);
+                *reinterpret_cast<u32x4_t*>(xw_lds + (r * 16 + (li ^ r)) * 16) = u32x4_t{p[0], p[1], p[2], p[3]};
             }
             u32x4_t a[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xw_lds + (li * 16 + ((4 * t + lb) ^ li)) * 16);
-                const uint32_t xw[4] = {v.x, v.y, v.z, v.w};
-                uint32_t p[4];
-                x_pairs_for_biased(xw, p);
-                a[t] = u32x4_t{p[0], p[1], p[2], p[3]};
-            }
+            for (int t = 0; t < 4; ++t)
+                a[t] = *reinterpret_cast<const u32x4_t*>(xw_lds + (li * 16 + ((4 * t + lb) ^ li)) * 16);
             f32x4_t sx = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int t = 0; t < 4; ++t) sx = mfma(a[t], ones, sx);

@@ -123,11 +123,13 @@ __device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
 // x pairs matching int4_word_biased_pairs: from the eight bf16 x[8p .. 8p+7]
 // held as four words (x0,x1), (x2,x3), (x4,x5), (x6,x7), build
 // (x_j, x_{j+4}) for j = 0..3.
+// Each output is one byte select (v_perm_b32: selector bytes 0-3 pick from
+// the second operand, 4-7 from the first).
 __device__ __forceinline__ void x_pairs_for_biased(const uint32_t xw[4], uint32_t out[4]) {
-    out[0] = (xw[0] & 0xFFFFu) | (xw[2] << 16);
-    out[1] = (xw[0] >> 16) | (xw[2] & 0xFFFF0000u);
-    out[2] = (xw[1] & 0xFFFFu) | (xw[3] << 16);
-    out[3] = (xw[1] >> 16) | (xw[3] & 0xFFFF0000u);
+    out[0] = __builtin_amdgcn_perm(xw[2], xw[0], 0x05040100u);  // low halves
+    out[1] = __builtin_amdgcn_perm(xw[2], xw[0], 0x07060302u);  // high halves
+    out[2] = __builtin_amdgcn_perm(xw[3], xw[1], 0x05040100u);
+    out[3] = __builtin_amdgcn_perm(xw[3], xw[1], 0x07060302u);
 }
 
 // FP32 dequantisation of one word, as the prefill GEMM computes it:
