@@ -186,14 +186,19 @@ __global__ __launch_bounds__(kThreads) void moe_gemv_fp4_kernel(MoeFc f, const i
 // [0, b1) of each slot run the first FC, the rest the second.  One launch
 // instead of two: the second FC's weights stream while the first's finish,
 // with one ramp and one tail.
-template <int CPL1, int CPL2, int RPT>
+template <int CPL1, int CPL2, int RPT1, int RPT2>
 __global__ __launch_bounds__(kThreads) void moe_gemv2_fp4_kernel(MoeFc f1, MoeFc f2, int b1,
                                                                  const int32_t* __restrict__ ids,
                                                                  int num_experts) {
-    __shared__ float part[1][4 * RPT];
+    constexpr int R = RPT1 > RPT2 ? RPT1 : RPT2;
+    __shared__ float part[4 * R];
     __shared__ u32x4_t xs[4 * (CPL1 > CPL2 ? CPL1 : CPL2) * kWave];
-    if ((int)blockIdx.x < b1) moe_gemv_rows<1, CPL1, RPT>(f1, ids, num_experts, blockIdx.x, blockIdx.y, part, xs);
-    else moe_gemv_rows<1, CPL2, RPT>(f2, ids, num_experts, blockIdx.x - b1, blockIdx.y, part, xs);
+    if ((int)blockIdx.x < b1)
+        moe_gemv_rows<1, CPL1, RPT1>(f1, ids, num_experts, blockIdx.x, blockIdx.y,
+                                     *reinterpret_cast<float(*)[1][4 * RPT1]>(part), xs);
+    else
+        moe_gemv_rows<1, CPL2, RPT2>(f2, ids, num_experts, blockIdx.x - b1, blockIdx.y,
+                                     *reinterpret_cast<float(*)[1][4 * RPT2]>(part), xs);
 }
 
 template <int S, int CPL, int RPT>
@@ -214,6 +219,7 @@ hipError_t launch_rpt(const void* x, int64_t x_stride, const uint8_t* qw, const 
                       const int32_t* ids, void* y, int E, int num_experts, int C, int N,
                       hipStream_t stream) {
     switch (moe_gemv_rows_per_wave(E, C * 32, N)) {
+        case 8: return launch_shape<S, CPL, 8>(x, x_stride, qw, s, ids, y, E, num_experts, C, N, stream);
         case 4: return launch_shape<S, CPL, 4>(x, x_stride, qw, s, ids, y, E, num_experts, C, N, stream);
         case 2: return launch_shape<S, CPL, 2>(x, x_stride, qw, s, ids, y, E, num_experts, C, N, stream);
         default: return launch_shape<S, CPL, 1>(x, x_stride, qw, s, ids, y, E, num_experts, C, N, stream);
@@ -240,23 +246,33 @@ hipError_t launch_moe_gemv_fp4(const void* x, int64_t x_stride, const uint8_t* q
 
 namespace {
 
-template <int CPL1, int CPL2, int RPT>
+template <int CPL1, int CPL2, int RPT1, int RPT2>
 hipError_t launch_pair(const MoeFc& f1, const MoeFc& f2, const int32_t* ids, int E, int num_experts,
                        hipStream_t stream) {
-    const int b1 = (f1.N + 4 * RPT - 1) / (4 * RPT), b2 = (f2.N + 4 * RPT - 1) / (4 * RPT);
-    moe_gemv2_fp4_kernel<CPL1, CPL2, RPT><<<dim3((unsigned)(b1 + b2), (unsigned)E), kThreads, 0, stream>>>(
+    const int b1 = (f1.N + 4 * RPT1 - 1) / (4 * RPT1), b2 = (f2.N + 4 * RPT2 - 1) / (4 * RPT2);
+    moe_gemv2_fp4_kernel<CPL1, CPL2, RPT1, RPT2><<<dim3((unsigned)(b1 + b2), (unsigned)E), kThreads, 0, stream>>>(
         f1, f2, b1, ids, num_experts);
     return hipGetLastError();
 }
 
-template <int RPT>
-hipError_t launch_pair_rpt(const MoeFc& f1, const MoeFc& f2, const int32_t* ids, int E, int num_experts,
+template <int RPT1, int RPT2>
+hipError_t launch_pair_cpl(const MoeFc& f1, const MoeFc& f2, const int32_t* ids, int E, int num_experts,
                            hipStream_t stream) {
     switch (row_split(f1.C).cpl * 16 + row_split(f2.C).cpl) {
-        case 1 * 16 + 1: return launch_pair<1, 1, RPT>(f1, f2, ids, E, num_experts, stream);
-        case 1 * 16 + 2: return launch_pair<1, 2, RPT>(f1, f2, ids, E, num_experts, stream);
-        case 2 * 16 + 1: return launch_pair<2, 1, RPT>(f1, f2, ids, E, num_experts, stream);
-        default: return launch_pair<2, 2, RPT>(f1, f2, ids, E, num_experts, stream);
+        case 1 * 16 + 1: return launch_pair<1, 1, RPT1, RPT2>(f1, f2, ids, E, num_experts, stream);
+        case 1 * 16 + 2: return launch_pair<1, 2, RPT1, RPT2>(f1, f2, ids, E, num_experts, stream);
+        case 2 * 16 + 1: return launch_pair<2, 1, RPT1, RPT2>(f1, f2, ids, E, num_experts, stream);
+        default: return launch_pair<2, 2, RPT1, RPT2>(f1, f2, ids, E, num_experts, stream);
+    }
+}
+
+template <int RPT1>
+hipError_t launch_pair_rpt(int rpt2, const MoeFc& f1, const MoeFc& f2, const int32_t* ids, int E,
+                           int num_experts, hipStream_t stream) {
+    switch (rpt2) {
+        case 8: return launch_pair_cpl<RPT1, 8>(f1, f2, ids, E, num_experts, stream);
+        case 4: return launch_pair_cpl<RPT1, 4>(f1, f2, ids, E, num_experts, stream);
+        default: return launch_pair_cpl<RPT1, 2>(f1, f2, ids, E, num_experts, stream);
     }
 }
 
@@ -265,11 +281,14 @@ hipError_t launch_pair_rpt(const MoeFc& f1, const MoeFc& f2, const int32_t* ids,
 hipError_t launch_moe_gemv2_fp4(const MoeFcArgs& a, const MoeFcArgs& b, const int32_t* ids, int E, int num_experts,
                                 hipStream_t stream) {
     // One launch when both rows fit one wave's slice (K <= 4096) and both
-    // shapes take the same rows per wave (2 or 4); else the two FCs one after
-    // the other (same results, bit for bit).
+    // shapes take 2, 4 or 8 rows per wave (each FC its own, as in its own
+    // launch); else the two FCs one after the other (same results, bit for
+    // bit).  The first FC's workgroups come first in the grid, so the
+    // launch's tail is the second FC's.
     const int Ca = a.K / 32, Cb = b.K / 32;
     const int pa = moe_gemv_rows_per_wave(E, a.K, a.N), pb = moe_gemv_rows_per_wave(E, b.K, b.N);
-    if (row_split(Ca).slices != 1 || row_split(Cb).slices != 1 || pa != pb || (pa != 2 && pa != 4)) {
+    auto pair_rpt = [](int p) { return p == 2 || p == 4 || p == 8; };
+    if (row_split(Ca).slices != 1 || row_split(Cb).slices != 1 || !pair_rpt(pa) || !pair_rpt(pb)) {
         hipError_t err = launch_moe_gemv_fp4(a.x, a.x_stride, a.qw, a.s, ids, a.y, E, num_experts, a.K, a.N, stream);
         if (err != hipSuccess) return err;
         return launch_moe_gemv_fp4(b.x, b.x_stride, b.qw, b.s, ids, b.y, E, num_experts, b.K, b.N, stream);
@@ -278,8 +297,11 @@ hipError_t launch_moe_gemv2_fp4(const MoeFcArgs& a, const MoeFcArgs& b, const in
                    static_cast<const uint16_t*>(a.s), static_cast<uint16_t*>(a.y), Ca, a.N};
     const MoeFc f2{static_cast<const u32x4_t*>(b.x), (long)(b.x_stride / 8), reinterpret_cast<const u32x4_t*>(b.qw),
                    static_cast<const uint16_t*>(b.s), static_cast<uint16_t*>(b.y), Cb, b.N};
-    if (pa == 4) return launch_pair_rpt<4>(f1, f2, ids, E, num_experts, stream);
-    return launch_pair_rpt<2>(f1, f2, ids, E, num_experts, stream);
+    switch (pa) {
+        case 8: return launch_pair_rpt<8>(pb, f1, f2, ids, E, num_experts, stream);
+        case 4: return launch_pair_rpt<4>(pb, f1, f2, ids, E, num_experts, stream);
+        default: return launch_pair_rpt<2>(pb, f1, f2, ids, E, num_experts, stream);
+    }
 }
 
 }  // namespace w4

@@ -41,7 +41,7 @@ bool tune_param_valid(int kernel, int param) {
         case W4_TUNE_GEMV_ROWS2: return param == 1 || param == 2 || param == 4;
         case W4_TUNE_GEMM_SMALL_M: return param == 1 || param == 2 || param == 4;
         case W4_TUNE_GEMM: return param >= 1 && param <= 16;
-        case W4_TUNE_MOE_GEMV: return param == 1 || param == 2 || param == 4;
+        case W4_TUNE_MOE_GEMV: return param == 1 || param == 2 || param == 4 || param == 8;
         default: return false;
     }
 }
@@ -103,7 +103,7 @@ int gemm_splits_rule(int M, int K, int N) {
 // workgroups over all slots.
 int moe_gemv_rows_per_wave_rule(int E, int K, int N) {
     const int T = 4 / row_split(K / 32).slices;
-    for (int rpt = 4; rpt > 1; rpt /= 2)
+    for (int rpt = 8; rpt > 1; rpt /= 2)
         if ((long)E * ((N + T * rpt - 1) / (T * rpt)) >= 512) return rpt;
     return 1;
 }

@@ -270,7 +270,7 @@ W4_API w4_status w4_repack_gptq(const int32_t* qw_kn, const void* s_gn, const vo
  *   W4_TUNE_GEMM_SMALL_M  w4_gemm at 3 <= M <= 16: weight rows per workgroup / 16, 1, 2 or 4
  *   W4_TUNE_GEMM          w4_gemm at M > 16: K splits, 1 .. 16 (at most K / 128); it sets
  *                         w4_gemm_workspace_bytes()
- *   W4_TUNE_MOE_GEMV      w4_moe_gemv: weight rows per wave, 1, 2 or 4 (M = the slot count E)
+ *   W4_TUNE_MOE_GEMV      w4_moe_gemv: weight rows per wave, 1, 2, 4 or 8 (M = the slot count E)
  * w4_tune_param returns the parameter a call of shape (M, K, N) would launch
  * with, or -1 for an unknown kernel.  w4_tune_force makes every later call of
  * a kernel family launch with ``param`` (0 restores the table), for tuning

@@ -299,7 +299,8 @@ def test_tune_rules_outside_the_table():
     assert lib.w4_tune_param(3, 128, 2048, 64) == 16  # one tile: 16 splits (= K / 128)
     assert lib.w4_tune_param(3, 128, 256, 64) == 2   # at most one group per split
     assert lib.w4_tune_param(3, 1024, 3840, 1 << 14) == 1
-    assert lib.w4_tune_param(4, 6, 256, 1 << 16) == 4
+    assert lib.w4_tune_param(4, 6, 256, 1 << 16) == 8
+    assert lib.w4_tune_param(4, 6, 256, 1 << 11) == 4
     assert lib.w4_tune_param(9, 1, 256, 64) == -1
 
 

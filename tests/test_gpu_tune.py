@@ -86,7 +86,7 @@ def test_prefill_k_splits(splits):
     check_outputs(_run_gemm(lin, x_bits, M, K, N), y_ref, xn, wmax, f"prefill splits={splits}")
 
 
-@pytest.mark.parametrize("rpt", [1, 2, 4])
+@pytest.mark.parametrize("rpt", [1, 2, 4, 8])
 @pytest.mark.parametrize("K,N,shared", [(4096, 200, True), (2048, 130, False)])
 def test_moe_gemv_rows_per_wave(rpt, K, N, shared):
     w4.w4_tune_force("moe_gemv", rpt)
