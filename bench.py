@@ -320,8 +320,9 @@ def extra_workloads(w4, host, si, torch, rf):
                                                        "GBps": round(nb / (us2 * 1e-6) / 1e9, 1)}}
     log(f"FP4 MoE 6 experts x 2 FC: {us:.1f} us/token in one launch ({us2:.1f} in two), {gbps:.0f} GB/s")
 
-    # grouped FP4 expert GEMM (w4_moe_gemm): 6 experts x 16 tokens each, FC1 then FC2,
-    # a fresh id set per call (the same 64 id sets)
+    # grouped FP4 expert GEMM: 6 experts x 16 tokens each, FC1 and FC2 (FC2 reads its own
+    # activations) in one w4_moe_gemm2 launch, and as two w4_moe_gemm launches; a fresh
+    # id set per call (the same 64 id sets)
     rows = 16
     R = si.MOE_SLOTS * rows
     row_start = torch.arange(0, R + 1, rows, dtype=torch.int32, device="cuda")
@@ -330,23 +331,32 @@ def extra_workloads(w4, host, si, torch, rf):
     yg1 = torch.empty(R, N1, dtype=torch.bfloat16, device="cuda")
     yg2 = torch.empty(R, N2, dtype=torch.bfloat16, device="cuda")
 
-    def moe_groups():
+    def moe_groups():  # one launch per id set: both FCs (w4_moe_gemm2)
+        for t in range(tokens):
+            w4.w4_moe_gemm2((xg1, pools[0]["qw"], pools[0]["s"], yg1), (xg2, pools[1]["qw"], pools[1]["s"], yg2),
+                            row_start, ids[t], rows, stream=stream)
+
+    def moe_groups_two():  # two launches per id set
         for t in range(tokens):
             w4.w4_moe_gemm(xg1, row_start, ids[t], pools[0]["qw"], pools[0]["s"], yg1, rows, stream=stream)
             w4.w4_moe_gemm(xg2, row_start, ids[t], pools[1]["qw"], pools[1]["s"], yg2, rows, stream=stream)
 
     g = capture(w4, torch, stream, moe_groups)
-    ms = time_graph(torch, lambda: g.replay(stream), stream, reps=10)
-    us = ms * 1e3 / tokens
+    us = time_graph(torch, lambda: g.replay(stream), stream, reps=10) * 1e3 / tokens
+    g.destroy()
+    g = capture(w4, torch, stream, moe_groups_two)
+    us2 = time_graph(torch, lambda: g.replay(stream), stream, reps=10) * 1e3 / tokens
+    g.destroy()
     nb = (si.MOE_SLOTS * (rf.fp4_expert_bytes(K1, N1) + rf.fp4_expert_bytes(K2, N2))
           + 2 * R * (K1 + N1 + K2 + N2))
     fl = 2.0 * R * (K1 * N1 + K2 * N2)
     out["moe_fp4_grouped_gemm_6x16rows_2fc"] = {
         "us_per_call_pair": round(us, 2), "GBps": round(nb / (us * 1e-6) / 1e9, 1),
         "frac_hbm": round(nb / (us * 1e-6) / 1e9 / rf.HBM_PEAK_GBPS, 4),
-        "TFLOPs": round(fl / (us * 1e-6) / 1e12, 2), "bytes": nb}
-    g.destroy()
-    log(f"FP4 grouped GEMM 6 experts x 16 rows x 2 FC: {us:.1f} us, {nb / (us * 1e-6) / 1e9:.0f} GB/s")
+        "TFLOPs": round(fl / (us * 1e-6) / 1e12, 2), "bytes": nb,
+        "two_launches": {"us_per_call_pair": round(us2, 2), "GBps": round(nb / (us2 * 1e-6) / 1e9, 1)}}
+    log(f"FP4 grouped GEMM 6 experts x 16 rows x 2 FC: {us:.1f} us in one launch ({us2:.1f} in two), "
+        f"{nb / (us * 1e-6) / 1e9:.0f} GB/s")
     return out
 
 

@@ -22,7 +22,7 @@ import torch
 
 __all__ = [
     "W4Error", "lib", "LIB_PATH", "w4_abi_version", "w4_status_string", "w4_last_error",
-    "w4_gemv", "w4_gemm", "w4_gemm_workspace_bytes", "w4_moe_gemv", "w4_moe_gemv2", "w4_moe_gemm",
+    "w4_gemv", "w4_gemm", "w4_gemm_workspace_bytes", "w4_moe_gemv", "w4_moe_gemv2", "w4_moe_gemm", "w4_moe_gemm2",
     "w4_graph_begin", "w4_graph_end", "w4_graph_replay", "w4_graph_destroy", "W4Graph",
     "w4_dequant_int4", "w4_dequant_fp4", "w4_int4_gemv_operands", "INT4_GROUP", "FP4_GROUP", "GEMV_MAX_K",
     "GemvDesc", "W4Chain", "w4_chain_workspace_bytes", "w4_chain_create", "w4_chain_run",
@@ -64,6 +64,12 @@ class MoeFc(ctypes.Structure):
                 ("s_fp4", ctypes.c_void_p), ("y", ctypes.c_void_p), ("K", ctypes.c_int), ("N", ctypes.c_int)]
 
 
+class MoeGemmFc(ctypes.Structure):
+    """struct w4_moe_gemm_fc (include/w4.h)."""
+    _fields_ = [("x", ctypes.c_void_p), ("qw_fp4", ctypes.c_void_p), ("s_fp4", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("K", ctypes.c_int), ("N", ctypes.c_int)]
+
+
 # name -> (restype, argtypes), mirroring include/w4.h
 SIGNATURES = {
     "w4_abi_version": (_i32, []),
@@ -76,6 +82,8 @@ SIGNATURES = {
     "w4_moe_gemv": (_i32, [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "w4_moe_gemv2": (_i32, [ctypes.POINTER(MoeFc), ctypes.POINTER(MoeFc), _vp, _i32, _i32, _vp]),
     "w4_moe_gemm": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "w4_moe_gemm2": (_i32, [ctypes.POINTER(MoeGemmFc), ctypes.POINTER(MoeGemmFc), _vp, _vp, _i32, _i32, _i32, _i32,
+                            _vp]),
     "w4_graph_begin": (_i32, [_vp]),
     "w4_graph_end": (_i32, [_vp, ctypes.POINTER(_vp)]),
     "w4_graph_replay": (_i32, [_vp, _vp]),
@@ -229,6 +237,39 @@ def w4_moe_gemm(x, row_start, expert_ids, qw_fp4, s_fp4, y, max_rows: int, strea
                            _dev(s_fp4, "s_fp4", _BF16), _dev(y, "y", _BF16), R, E, int(max_rows), num_experts, K, N,
                            _stream(stream)), "w4_moe_gemm")
     return y
+
+
+def _moe_gemm_fc(x, qw_fp4, s_fp4, y, R):
+    if qw_fp4.dim() != 3:
+        raise ValueError("qw_fp4 must be [experts, N, K/2]")
+    num_experts, N, half_k = qw_fp4.shape
+    K = 2 * half_k
+    if tuple(s_fp4.shape) != (num_experts, N, K // FP4_GROUP):
+        raise ValueError(f"s_fp4 must be [experts, N, K/32]; got {tuple(s_fp4.shape)}")
+    if tuple(x.shape) != (R, K):
+        raise ValueError(f"x must be [R, K] = {(R, K)}; got {tuple(x.shape)}")
+    if tuple(y.shape) != (R, N):
+        raise ValueError(f"y must be [R, N] = {(R, N)}; got {tuple(y.shape)}")
+    fc = MoeGemmFc(_dev(x, "x", _BF16), _dev(qw_fp4, "qw_fp4", _U8), _dev(s_fp4, "s_fp4", _BF16), _dev(y, "y", _BF16),
+                   K, N)
+    return fc, num_experts
+
+
+def w4_moe_gemm2(fc1, fc2, row_start, expert_ids, max_rows: int, stream=None):
+    """Two grouped FP4 expert GEMMs over the same groups in one launch; ``fc1`` and ``fc2`` are
+    ``(x, qw_fp4, s_fp4, y)`` as for ``w4_moe_gemm`` (their inputs must not depend on each other)."""
+    R = fc1[0].shape[0]
+    E = expert_ids.numel()
+    if row_start.numel() != E + 1:
+        raise ValueError(f"row_start must have E + 1 = {E + 1} entries")
+    f1, n1 = _moe_gemm_fc(*fc1, R)
+    f2, n2 = _moe_gemm_fc(*fc2, R)
+    if n1 != n2:
+        raise ValueError("both expert pools must hold the same number of experts")
+    _check(lib.w4_moe_gemm2(ctypes.byref(f1), ctypes.byref(f2), _dev(row_start, "row_start", _I32),
+                            _dev(expert_ids, "expert_ids", _I32), R, E, int(max_rows), n1, _stream(stream)),
+           "w4_moe_gemm2")
+    return fc1[3], fc2[3]
 
 
 def w4_moe_gemv(x, qw_fp4, s_fp4, expert_ids, y, stream=None) -> torch.Tensor:

@@ -61,24 +61,46 @@ struct Slot {
     u32x4_t a[4];    // activation chunk (lane % 16) of rows lane / 16 + 4 i
 };
 
+// One FC of the grouped GEMM, as w4_moe_gemm takes it.
+struct GemmFc {
+    const uint16_t* x;  // bf16 [R][K]
+    const uint8_t* qw;  // [num_experts][N][K/2]
+    const uint16_t* s;  // bf16 [num_experts][N][K/32]
+    uint16_t* y;        // bf16 [R][N]
+    int K, N;
+};
+
+// LDS of one workgroup: the scales of its rows, then each wave's activation
+// tile (in the K loop) or partial sums (after it).
 template <int kCB>
-__global__ __launch_bounds__(kThreads) void moe_gemm_fp4_kernel(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ row_start, const int32_t* __restrict__ ids,
-    const uint8_t* __restrict__ qw, const uint16_t* __restrict__ s, uint16_t* __restrict__ y, int R,
-    int num_experts, int K, int N) {
+constexpr int tile_lds_bytes() {
     constexpr int kBN = 16 * kCB;
     constexpr int kSBytes = kBN * kMaxSteps * 4 * 2;      // bf16 scales [kBN][K / 32]
     constexpr int kXBytes = kWaves * 16 * kStep * 2;      // each wave's 16 x 128 activation tile
     constexpr int kRedBytes = kWaves * kCB * kWave * 16;  // each wave's 16 x kBN partial sums
-    constexpr int kTail = kRedBytes > kXBytes ? kRedBytes : kXBytes;
-    static_assert(kSBytes + kTail <= 160 * 1024, "LDS budget of one gfx950 workgroup");
-    __shared__ __attribute__((aligned(16))) char lds[kSBytes + kTail];
+    return kSBytes + (kRedBytes > kXBytes ? kRedBytes : kXBytes);
+}
+
+// Weight-row tile bx (16 kCB rows) of FC f for slab blockIdx.y of group
+// blockIdx.z.
+template <int kCB>
+__device__ __forceinline__ void moe_gemm_tile(const GemmFc& f, const int32_t* __restrict__ row_start,
+                                              const int32_t* __restrict__ ids, int R, int num_experts, int bx,
+                                              char* lds) {
+    constexpr int kBN = 16 * kCB;
+    constexpr int kSBytes = kBN * kMaxSteps * 4 * 2;
+    static_assert(tile_lds_bytes<kCB>() <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+    const uint16_t* __restrict__ x = f.x;
+    const uint8_t* __restrict__ qw = f.qw;
+    const uint16_t* __restrict__ s = f.s;
+    uint16_t* __restrict__ y = f.y;
+    const int K = f.K, N = f.N;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int li = lane & 15, lb = lane >> 4;
-    const int n0 = blockIdx.x * kBN;
+    const int n0 = bx * kBN;
     const int group = blockIdx.z;
 
     // The group's rows, clamped into x and y: [r0, r1).
@@ -228,28 +250,76 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp4_kernel(
     }
 }
 
+template <int kCB>
+__global__ __launch_bounds__(kThreads) void moe_gemm_fp4_kernel(GemmFc f, const int32_t* __restrict__ row_start,
+                                                                const int32_t* __restrict__ ids, int R,
+                                                                int num_experts) {
+    __shared__ __attribute__((aligned(16))) char lds[tile_lds_bytes<kCB>()];
+    moe_gemm_tile<kCB>(f, row_start, ids, R, num_experts, blockIdx.x, lds);
+}
+
+// Two FCs over the same groups in one launch: weight-row tiles [0, b1) of
+// each slab run the first FC, the rest the second.
+template <int kCB1, int kCB2>
+__global__ __launch_bounds__(kThreads) void moe_gemm2_fp4_kernel(GemmFc f1, GemmFc f2, int b1,
+                                                                 const int32_t* __restrict__ row_start,
+                                                                 const int32_t* __restrict__ ids, int R,
+                                                                 int num_experts) {
+    constexpr int kBytes = tile_lds_bytes<kCB1>() > tile_lds_bytes<kCB2>() ? tile_lds_bytes<kCB1>()
+                                                                             : tile_lds_bytes<kCB2>();
+    __shared__ __attribute__((aligned(16))) char lds[kBytes];
+    if ((int)blockIdx.x < b1) moe_gemm_tile<kCB1>(f1, row_start, ids, R, num_experts, blockIdx.x, lds);
+    else moe_gemm_tile<kCB2>(f2, row_start, ids, R, num_experts, blockIdx.x - b1, lds);
+}
+
+// 32 weight rows per workgroup (two workgroups per compute unit) when that
+// gives at least 240 workgroups for groups of max_rows rows, else 16.
+// Measured on 6 experts x 16 rows, FC1 and FC2: 26.1 us per pair at 32 rows,
+// 29.3 at 16, 30.4 at 64 (one workgroup per compute unit).
+int column_blocks(int N, int slabs, int E) { return (long)((N + 31) / 32) * slabs * E >= 240 ? 2 : 1; }
+
 }  // namespace
 
 hipError_t launch_moe_gemm_fp4(const void* x, const int32_t* row_start, const int32_t* ids, const uint8_t* qw,
                                const void* s, void* y, int R, int E, int max_rows, int num_experts, int K, int N,
                                hipStream_t stream) {
-    const uint16_t* xb = static_cast<const uint16_t*>(x);
-    const uint16_t* sb = static_cast<const uint16_t*>(s);
-    uint16_t* yb = static_cast<uint16_t*>(y);
+    const GemmFc f{static_cast<const uint16_t*>(x), qw, static_cast<const uint16_t*>(s), static_cast<uint16_t*>(y),
+                   K, N};
     const unsigned slabs = (unsigned)((max_rows + 15) / 16);
-    // 32 weight rows per workgroup (two workgroups per compute unit) when
-    // that gives at least 240 workgroups for groups of max_rows rows, else
-    // 16.  Measured on 6 experts x 16 rows, FC1 and FC2: 26.1 us per pair
-    // at 32 rows, 29.3 at 16, 30.4 at 64 (one workgroup per compute unit).
     auto launch = [&](auto cb) {
         constexpr int kCB = decltype(cb)::value;
         const dim3 grid((unsigned)((N + 16 * kCB - 1) / (16 * kCB)), slabs, (unsigned)E);
-        moe_gemm_fp4_kernel<kCB><<<grid, kThreads, 0, stream>>>(xb, row_start, ids, qw, sb, yb, R, num_experts, K, N);
+        moe_gemm_fp4_kernel<kCB><<<grid, kThreads, 0, stream>>>(f, row_start, ids, R, num_experts);
         return hipGetLastError();
     };
-    const long per = (long)slabs * E;
-    if ((long)((N + 31) / 32) * per >= 240) return launch(std::integral_constant<int, 2>{});
+    if (column_blocks(N, (int)slabs, E) == 2) return launch(std::integral_constant<int, 2>{});
     return launch(std::integral_constant<int, 1>{});
+}
+
+hipError_t launch_moe_gemm2_fp4(const MoeGemmFcArgs& a, const MoeGemmFcArgs& b, const int32_t* row_start,
+                                const int32_t* ids, int R, int E, int max_rows, int num_experts,
+                                hipStream_t stream) {
+    const GemmFc f1{static_cast<const uint16_t*>(a.x), a.qw, static_cast<const uint16_t*>(a.s),
+                    static_cast<uint16_t*>(a.y), a.K, a.N};
+    const GemmFc f2{static_cast<const uint16_t*>(b.x), b.qw, static_cast<const uint16_t*>(b.s),
+                    static_cast<uint16_t*>(b.y), b.K, b.N};
+    const int slabs = (max_rows + 15) / 16;
+    // Each FC takes the tile width its own launch would (same bits).
+    auto launch = [&](auto cb1, auto cb2) {
+        constexpr int kCB1 = decltype(cb1)::value, kCB2 = decltype(cb2)::value;
+        const int b1 = (a.N + 16 * kCB1 - 1) / (16 * kCB1), b2 = (b.N + 16 * kCB2 - 1) / (16 * kCB2);
+        const dim3 grid((unsigned)(b1 + b2), (unsigned)slabs, (unsigned)E);
+        moe_gemm2_fp4_kernel<kCB1, kCB2><<<grid, kThreads, 0, stream>>>(f1, f2, b1, row_start, ids, R, num_experts);
+        return hipGetLastError();
+    };
+    using One = std::integral_constant<int, 1>;
+    using Two = std::integral_constant<int, 2>;
+    switch (column_blocks(a.N, slabs, E) * 16 + column_blocks(b.N, slabs, E)) {
+        case 2 * 16 + 2: return launch(Two{}, Two{});
+        case 2 * 16 + 1: return launch(Two{}, One{});
+        case 1 * 16 + 2: return launch(One{}, Two{});
+        default: return launch(One{}, One{});
+    }
 }
 
 }  // namespace w4

@@ -328,6 +328,66 @@ W4_API w4_status w4_moe_gemm(const void* x, const int32_t* row_start, const int3
     return err == hipSuccess ? W4_OK : hip_fail(err, fn);
 }
 
+W4_API w4_status w4_moe_gemm2(const w4_moe_gemm_fc* fc1, const w4_moe_gemm_fc* fc2, const int32_t* row_start,
+                              const int32_t* expert_ids, int R, int E, int max_rows, int num_experts,
+                              void* stream) {
+    const char* fn = "w4_moe_gemm2";
+    if (!fc1 || !fc2 || !row_start || !expert_ids)
+        return fail(W4_ERR_NULL, "%s: fc1, fc2, row_start and expert_ids must not be NULL", fn);
+    if (R < 0 || E < 0 || max_rows < 0)
+        return fail(W4_ERR_SHAPE, "%s: R = %d, E = %d, max_rows = %d must not be negative", fn, R, E, max_rows);
+    if (num_experts < 1) return fail(W4_ERR_ARG, "%s: num_experts = %d must be positive", fn, num_experts);
+    if (!aligned(row_start, 4) || !aligned(expert_ids, 4))
+        return fail(W4_ERR_ALIGN, "%s: row_start and expert_ids must be 4-byte aligned", fn);
+    const w4_moe_gemm_fc* fcs[2] = {fc1, fc2};
+    Range ys[2], ins[2][3];
+    for (int i = 0; i < 2; ++i) {
+        const w4_moe_gemm_fc& f = *fcs[i];
+        if (!f.x || !f.qw_fp4 || !f.s_fp4 || !f.y)
+            return fail(W4_ERR_NULL, "%s: fc%d: x, qw_fp4, s_fp4 and y must not be NULL", fn, i + 1);
+        if (f.N < 0) return fail(W4_ERR_SHAPE, "%s: fc%d: N = %d is negative", fn, i + 1, f.N);
+        if (f.K <= 0 || f.K % 128 != 0 || f.K > W4_MOE_GEMM_MAX_K)
+            return fail(W4_ERR_SHAPE, "%s: fc%d: K = %d must be a positive multiple of 128 up to %d", fn, i + 1, f.K,
+                        W4_MOE_GEMM_MAX_K);
+        if ((unsigned long long)f.N * (unsigned long long)(f.K / 2) > W4_GEMV_MAX_MATRIX_BYTES ||
+            (unsigned long long)R * (unsigned long long)f.K * 2ull > W4_GEMV_MAX_MATRIX_BYTES)
+            return fail(W4_ERR_SHAPE, "%s: fc%d: N * K / 2 or R * K * 2 exceeds %llu bytes", fn, i + 1,
+                        W4_GEMV_MAX_MATRIX_BYTES);
+        if (!aligned(f.x, 16) || !aligned(f.qw_fp4, 16))
+            return fail(W4_ERR_ALIGN, "%s: fc%d: x and qw_fp4 must be 16-byte aligned", fn, i + 1);
+        if (!aligned(f.s_fp4, 8) || !aligned(f.y, 2))
+            return fail(W4_ERR_ALIGN, "%s: fc%d: s_fp4 must be 8-byte and y 2-byte aligned", fn, i + 1);
+        ys[i] = range(f.y, (size_t)R * f.N * 2);
+        ins[i][0] = range(f.x, (size_t)R * f.K * 2);
+        ins[i][1] = range(f.qw_fp4, (size_t)num_experts * f.N * f.K / 2);
+        ins[i][2] = range(f.s_fp4, (size_t)num_experts * f.N * (f.K / 32) * 2);
+    }
+    const Range shared[2] = {range(expert_ids, (size_t)E * 4), range(row_start, (size_t)(E + 1) * 4)};
+    for (int i = 0; i < 2; ++i) {
+        for (const Range& r : shared)
+            if (overlap(ys[i], r)) return fail(W4_ERR_ALIAS, "%s: fc%d's y overlaps row_start or expert_ids", fn, i + 1);
+        for (int j = 0; j < 2; ++j)
+            for (const Range& r : ins[j])
+                if (overlap(ys[i], r))
+                    return fail(W4_ERR_ALIAS, "%s: fc%d's y overlaps an input of fc%d (the two FCs run together)",
+                                fn, i + 1, j + 1);
+    }
+    if (overlap(ys[0], ys[1])) return fail(W4_ERR_ALIAS, "%s: the two outputs overlap", fn);
+    if (R == 0 || E == 0 || max_rows == 0) return W4_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (fc1->N == 0 || fc2->N == 0) {  // one FC only
+        const w4_moe_gemm_fc& f = fc1->N == 0 ? *fc2 : *fc1;
+        if (f.N == 0) return W4_OK;
+        hipError_t err = w4::launch_moe_gemm_fp4(f.x, row_start, expert_ids, f.qw_fp4, f.s_fp4, f.y, R, E, max_rows,
+                                                 num_experts, f.K, f.N, st);
+        return err == hipSuccess ? W4_OK : hip_fail(err, fn);
+    }
+    const w4::MoeGemmFcArgs a{fc1->x, fc1->qw_fp4, fc1->s_fp4, fc1->y, fc1->K, fc1->N};
+    const w4::MoeGemmFcArgs b{fc2->x, fc2->qw_fp4, fc2->s_fp4, fc2->y, fc2->K, fc2->N};
+    hipError_t err = w4::launch_moe_gemm2_fp4(a, b, row_start, expert_ids, R, E, max_rows, num_experts, st);
+    return err == hipSuccess ? W4_OK : hip_fail(err, fn);
+}
+
 struct w4_graph {
     hipGraph_t graph;
     hipGraphExec_t exec;

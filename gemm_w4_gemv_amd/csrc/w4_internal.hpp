@@ -55,6 +55,17 @@ hipError_t launch_moe_gemv2_fp4(const MoeFcArgs& a, const MoeFcArgs& b, const in
 hipError_t launch_moe_gemm_fp4(const void* x, const int32_t* row_start, const int32_t* ids, const uint8_t* qw,
                                const void* s, void* y, int R, int E, int max_rows, int num_experts, int K, int N,
                                hipStream_t stream);
+// One FC of the grouped expert GEMM, as w4_moe_gemm takes it.
+struct MoeGemmFcArgs {
+    const void* x;
+    const uint8_t* qw;
+    const void* s;
+    void* y;
+    int K, N;
+};
+hipError_t launch_moe_gemm2_fp4(const MoeGemmFcArgs& a, const MoeGemmFcArgs& b, const int32_t* row_start,
+                                const int32_t* ids, int R, int E, int max_rows, int num_experts,
+                                hipStream_t stream);
 
 hipError_t launch_dequant_int4(const int32_t* qw, const void* s, const void* z, float* out_f32,
                                void* out_bf16, int K, int N, hipStream_t stream);

@@ -241,6 +241,35 @@ W4_API w4_status w4_moe_gemm(const void* x, const int32_t* row_start, const int3
                              int max_rows, int num_experts, int K, int N, void* stream);
 
 /*
+ * w4_moe_gemm2 -- two grouped FP4 expert GEMMs over the same groups (row
+ * ranges and expert ids) in one launch: the result of w4_moe_gemm(fc1) and
+ * w4_moe_gemm(fc2), bit for bit, for two FCs whose inputs are both ready
+ * (neither reads the other's output, e.g. the gate and up projections of the
+ * routed tokens).  "DeepSeek V4 Triton FP4 优化实战", "深度分析" items 2 and 4:
+ * each routed token runs 2 FC on its experts; one launch saves a launch's
+ * ramp and tail.
+ *   w4_moe_gemm_fc { x, qw_fp4, s_fp4, y, K, N } -- each field as for
+ *               w4_moe_gemm (fc1 and fc2 each have their own expert pool of
+ *               num_experts experts, their own K and N, and x [R][K])
+ *   row_start, expert_ids, R, E, max_rows, num_experts: as for w4_moe_gemm,
+ *               shared by both FCs
+ * Neither output may overlap any input of either FC, row_start, the ids or
+ * the other output.  A FC with N = 0 is skipped.
+ * Errors: as w4_moe_gemm.
+ */
+typedef struct w4_moe_gemm_fc {
+    const void* x;         /* device bf16 [R][K], 16-byte aligned */
+    const uint8_t* qw_fp4; /* device uint8 [num_experts][N][K/2], 16-byte aligned */
+    const void* s_fp4;     /* device bf16 [num_experts][N][K/32], 8-byte aligned */
+    void* y;               /* device bf16 [R][N], 2-byte aligned */
+    int K;
+    int N;
+} w4_moe_gemm_fc;
+W4_API w4_status w4_moe_gemm2(const w4_moe_gemm_fc* fc1, const w4_moe_gemm_fc* fc2, const int32_t* row_start,
+                              const int32_t* expert_ids, int R, int E, int max_rows, int num_experts,
+                              void* stream);
+
+/*
  * w4_repack_gptq -- import a weight stored in GPTQ's own K-major layout
  * ("Lab 5: Gemma4 端到端推理优化", section "量化正确性": GPTQ INT4, group 128,
  * asymmetric), once, at load time, into the layout every other entry point

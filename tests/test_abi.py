@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 27, names
+    assert len(names) == 28, names
     for name in names:
         assert hasattr(lib, name), f"libw4.so does not export {name}"
         assert name in w4.SIGNATURES, f"binding has no signature for {name}"
@@ -333,6 +333,36 @@ def test_repack_gptq_validation():
     assert rp(X, S, Z, X + 64, WSP, Y, 256, 64, 128, None) == ALIAS  # qw over qw_kn
     assert rp(X, S, Z, QW, QW + 64, Y, 256, 64, 128, None) == ALIAS  # s over qw
     assert rp(X, S, Z, QW, WSP, Y, 256, 0, 128, None) == OK  # empty: nothing launched
+
+
+def test_moe_gemm2_validation():
+    RS = IDS + 0x1000
+
+    def fc(x=X, qw=QW, s=S, y=Y, K=4096, N=2048):
+        return w4.MoeGemmFc(x, qw, s, y, K, N)
+    g2 = lib.w4_moe_gemm2
+    ok1 = fc()
+    ok2 = fc(x=X + 0x1000000, qw=QW + 0x1000000, s=S + 0x1000000, y=Y + 0x1000000, K=2048, N=4096)
+
+    def call(f1=ok1, f2=ok2, rs=RS, ids=IDS, R=96, E=6, mr=16, ne=64):
+        return g2(ctypes.byref(f1) if f1 is not None else None, ctypes.byref(f2) if f2 is not None else None,
+                  rs, ids, R, E, mr, ne, None)
+    assert call(f2=None) == NULL
+    assert call(rs=None) == NULL and call(ids=None) == NULL
+    assert call(f1=fc(s=None)) == NULL
+    assert call(f2=fc(K=2048 + 32)) == SHAPE       # not a multiple of 128
+    assert call(f1=fc(K=8192 + 128)) == SHAPE      # past W4_MOE_GEMM_MAX_K
+    assert call(f1=fc(N=-1)) == SHAPE and call(R=-1) == SHAPE and call(mr=-1) == SHAPE
+    assert call(ne=0) == ARG
+    assert call(f1=fc(qw=QW + 8)) == ALIGN
+    assert call(f2=fc(s=S + 4, K=2048, N=4096)) == ALIGN  # scales need 8-byte alignment
+    assert call(rs=RS + 2) == ALIGN
+    # an output over the other FC's input, over row_start, or over the other output
+    assert call(f2=fc(x=X + 0x1000000, qw=QW + 0x1000000, s=S + 0x1000000, y=X + 64, K=2048, N=4096)) == ALIAS
+    assert call(f1=fc(y=RS)) == ALIAS
+    assert call(f2=fc(x=X + 0x1000000, qw=QW + 0x1000000, s=S + 0x1000000, y=Y + 64, K=2048, N=4096)) == ALIAS
+    assert call(E=0) == OK and call(R=0) == OK and call(mr=0) == OK  # empty: nothing launched
+    assert "w4_moe_gemm2" in w4.w4_last_error()
 
 
 def test_moe_gemv2_validation():

@@ -888,6 +888,47 @@ def test_moe_gemm_multi_slab_invalid_id_and_untouched_rows():
     check_moe_groups(yv, x, pool, row_start[:4], ids[:3])
 
 
+def test_moe_gemm2_pair_equals_two_launches():
+    """w4_moe_gemm2: both FC shapes of the 64-expert pools over the same groups
+    (6 groups of 16 rows, as bench.py times them, then ragged groups with an empty
+    one and an id outside the pool) in one launch equal two w4_moe_gemm calls bit
+    for bit, NaNs included; FC1's outputs are checked against the oracle."""
+    pools = si.moe_pools()
+    dev = [host.fp4_tensors(p) for p in pools]
+    (K1, N1), (K2, N2) = si.MOE_FC
+    for case, (sizes, ids) in enumerate([([16] * 6, si.expert_ids(si.SEED, (53, 0)).tolist()),
+                                         ([5, 0, 16, 2, 9, 1], [7, 3, 70, 0, 63, 12])]):
+        row_start = np.concatenate([[0], np.cumsum(sizes)]).tolist()
+        R, mr = row_start[-1], max(sizes)
+        print(f"moe_gemm2 case {case}: rows={sizes} ids={ids}", flush=True)
+        x1 = si.bf16_normal(si.SEED, (53, case, 1), (R, K1))
+        x2 = si.bf16_normal(si.SEED, (53, case, 2), (R, K2))
+        rs = torch.tensor(row_start, dtype=torch.int32, device=DEV)
+        idt = torch.tensor(ids, dtype=torch.int32, device=DEV)
+        xt1, xt2 = host.bf16_tensor(x1), host.bf16_tensor(x2)
+        y1 = torch.full((R, N1), 0.5, dtype=torch.bfloat16, device=DEV)
+        y2 = torch.full((R, N2), 0.5, dtype=torch.bfloat16, device=DEV)
+        w4.w4_moe_gemm2((xt1, dev[0]["qw"], dev[0]["s"], y1), (xt2, dev[1]["qw"], dev[1]["s"], y2), rs, idt, mr)
+        r1, r2 = torch.full_like(y1, 0.5), torch.full_like(y2, 0.5)
+        w4.w4_moe_gemm(xt1, rs, idt, dev[0]["qw"], dev[0]["s"], r1, mr)
+        w4.w4_moe_gemm(xt2, rs, idt, dev[1]["qw"], dev[1]["s"], r2, mr)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), r1.view(torch.int16)), f"case {case}: FC1 differs from its own launch"
+        assert torch.equal(y2.view(torch.int16), r2.view(torch.int16)), f"case {case}: FC2 differs from its own launch"
+        valid = [e for e, i in enumerate(ids) if 0 <= i < si.MOE_POOL]
+        yv1 = host.bf16_values(y1)
+        for e in range(len(ids)):
+            if e not in valid:
+                assert np.all(np.isnan(yv1[row_start[e]:row_start[e + 1]]))
+        keep = [e for e in valid]
+        rs_v = [0]
+        rows = []
+        for e in keep:
+            rows.extend(range(row_start[e], row_start[e + 1]))
+            rs_v.append(len(rows))
+        check_moe_groups(yv1[rows], x1[rows], pools[0], rs_v, [ids[e] for e in keep])
+
+
 def test_moe_gemm_row_table_clamped():
     """Group bounds outside [0, R] are clamped on the device: a start below 0 reads
     as 0, an end past R as R, and an end below its start as an empty group."""
