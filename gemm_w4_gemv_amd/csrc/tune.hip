@@ -60,13 +60,13 @@ int tuned_param(int kernel, int M, int K, int N, int rule) {
 
 void tune_force(int kernel, int param) { g_forced[kernel].store(param, std::memory_order_relaxed); }
 
-// Rows per wave of the GEMV: the most (8, 4, 2, 1) that still launch 256
+// Rows per wave of the GEMV: the most (8, 4, 2, 1) that still launch 240
 // workgroups for a matrix under 16 MB (512 above).  Fewer, larger workgroups
 // cost less per launch; more of them keep more loads in flight.
 int gemv_rows_per_wave_rule(int K, int N) {
     const int C = K / 32;
     const int T = 4 / row_split(C).slices;
-    const long min_blocks = (size_t)N * (size_t)C * 16u < ((size_t)16 << 20) ? 256 : 512;
+    const long min_blocks = (size_t)N * (size_t)C * 16u < ((size_t)16 << 20) ? 240 : 512;
     for (int rpt = 8; rpt > 1; rpt /= 2)
         if ((N + T * rpt - 1) / (T * rpt) >= min_blocks) return rpt;
     return 1;
