@@ -945,9 +945,10 @@ def test_moe_gemm_row_table_clamped():
 
 
 def test_graph_replays_of_gemm_paths_equal_eager():
-    """The tiled GEMM (split K), the small-M GEMM and the grouped FP4 GEMM captured
-    in one HIP graph: five replays, with eager work and synchronisations between
-    them and the outputs cleared before each, all equal the eager results bit for bit."""
+    """The tiled GEMM (split K), the small-M GEMM, the grouped FP4 GEMM and the
+    grouped pair (w4_moe_gemm2) captured in one HIP graph: five replays, with eager
+    work and synchronisations between them and the outputs cleared before each, all
+    equal the eager results bit for bit."""
     stream = torch.cuda.Stream()
     lin = si.int4_linear(25, (1,), 2048, 192)
     t = host.int4_tensors(lin)
@@ -963,16 +964,24 @@ def test_graph_replays_of_gemm_paths_equal_eager():
     ym = torch.empty(30, 80, dtype=torch.bfloat16, device=DEV)
     rs = torch.tensor([0, 7, 7, 23, 30], dtype=torch.int32, device=DEV)
     ids = torch.tensor([5, 0, 2, 3], dtype=torch.int32, device=DEV)
+    pool2 = host.fp4_tensors(si.fp4_pool(25, (6,), 6, 256, 144))
+    xm2 = host.bf16_tensor(si.bf16_normal(25, (7,), (30, 256)))
+    yp1 = torch.empty(30, 80, dtype=torch.bfloat16, device=DEV)
+    yp2 = torch.empty(30, 144, dtype=torch.bfloat16, device=DEV)
 
     def body():
         w4.w4_gemm(xb, t["qw"], t["s"], t["z"], yb, workspace=ws, stream=stream)
         w4.w4_gemm(xs, t["qw"], t["s"], t["z"], ys, stream=stream)
         w4.w4_moe_gemm(xm, rs, ids, pool["qw"], pool["s"], ym, 16, stream=stream)
+        w4.w4_moe_gemm2((xm, pool["qw"], pool["s"], yp1), (xm2, pool2["qw"], pool2["s"], yp2), rs, ids, 16,
+                        stream=stream)
 
+    outs = (yb, ys, ym, yp1, yp2)
     with torch.cuda.stream(stream):
         body()
     stream.synchronize()
-    ref = [y.clone() for y in (yb, ys, ym)]
+    ref = [y.clone() for y in outs]
+    assert torch.equal(yp1.view(torch.int16), ym.view(torch.int16))  # the pair's FC1 is w4_moe_gemm's call
     torch.cuda.synchronize()
     w4.w4_graph_begin(stream)
     try:
@@ -981,12 +990,12 @@ def test_graph_replays_of_gemm_paths_equal_eager():
         g = w4.w4_graph_end(stream)
     try:
         for rep in range(5):
-            for y in (yb, ys, ym):
+            for y in outs:
                 y.zero_()
             torch.cuda.synchronize()
             g.replay(stream)
             stream.synchronize()
-            for y, r in zip((yb, ys, ym), ref):
+            for y, r in zip(outs, ref):
                 assert torch.equal(y.view(torch.int16), r.view(torch.int16)), f"replay {rep}"
             junk = torch.randn(1 << 20, device=DEV) * 2  # unrelated eager work between replays
             torch.cuda.synchronize()
