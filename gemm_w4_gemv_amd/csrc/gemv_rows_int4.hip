@@ -208,6 +208,7 @@ template <int S, int CPL, int MX>
 hipError_t launch_rpt(const void* x, const int32_t* qw, const void* s, const void* z, void* y, int M, int C,
                       int N, hipStream_t stream) {
     switch (gemv_rows2_rows_per_wave(C * 32, N)) {
+        case 8: return launch_shape<S, CPL, 8, MX>(x, qw, s, z, y, M, C, N, stream);
         case 4: return launch_shape<S, CPL, 4, MX>(x, qw, s, z, y, M, C, N, stream);
         case 2: return launch_shape<S, CPL, 2, MX>(x, qw, s, z, y, M, C, N, stream);
         default: return launch_shape<S, CPL, 1, MX>(x, qw, s, z, y, M, C, N, stream);

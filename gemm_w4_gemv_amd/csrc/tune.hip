@@ -38,7 +38,7 @@ int groups_of(int K) { return K / 128; }
 bool tune_param_valid(int kernel, int param) {
     switch (kernel) {
         case W4_TUNE_GEMV: return param == 1 || param == 2 || param == 4 || param == 8;
-        case W4_TUNE_GEMV_ROWS2: return param == 1 || param == 2 || param == 4;
+        case W4_TUNE_GEMV_ROWS2: return param == 1 || param == 2 || param == 4 || param == 8;
         case W4_TUNE_GEMM_SMALL_M: return param == 1 || param == 2 || param == 4;
         case W4_TUNE_GEMM: return param >= 1 && param <= 16;
         case W4_TUNE_MOE_GEMV: return param == 1 || param == 2 || param == 4 || param == 8;
@@ -72,10 +72,10 @@ int gemv_rows_per_wave_rule(int K, int N) {
     return 1;
 }
 
-// The two-row GEMV: the most (4, 2, 1) rows per wave that launch 512 workgroups.
+// The two-row GEMV: the most (8, 4, 2, 1) rows per wave that launch 512 workgroups.
 int gemv_rows2_rows_per_wave_rule(int K, int N) {
     const int T = 4 / row_split(K / 32).slices;
-    for (int rpt = 4; rpt > 1; rpt /= 2)
+    for (int rpt = 8; rpt > 1; rpt /= 2)
         if ((N + T * rpt - 1) / (T * rpt) >= 512) return rpt;
     return 1;
 }

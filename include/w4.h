@@ -295,7 +295,7 @@ W4_API w4_status w4_repack_gptq(const int32_t* qw_kn, const void* s_gn, const vo
  * launcher's rule.  Every value computes the same operation; summation order
  * (and so the last bits) may differ between values, never between runs.
  *   W4_TUNE_GEMV          w4_gemv, w4_gemm at M = 1: weight rows per wave, 1, 2, 4 or 8
- *   W4_TUNE_GEMV_ROWS2    w4_gemm at M = 2 (K <= 16384): weight rows per wave, 1, 2 or 4
+ *   W4_TUNE_GEMV_ROWS2    w4_gemm at M = 2 (K <= 16384): weight rows per wave, 1, 2, 4 or 8
  *   W4_TUNE_GEMM_SMALL_M  w4_gemm at 3 <= M <= 16: weight rows per workgroup / 16, 1, 2 or 4
  *   W4_TUNE_GEMM          w4_gemm at M > 16: K splits, 1 .. 16 (at most K / 128); it sets
  *                         w4_gemm_workspace_bytes()

@@ -61,7 +61,7 @@ def test_gemv_rows_per_wave(rpt, K, N):
     check_outputs(_run_gemm(lin, x_bits, 1, K, N), y_ref, xn, wmax, f"gemv rpt={rpt} K={K} N={N}")
 
 
-@pytest.mark.parametrize("rpt", [1, 2, 4])
+@pytest.mark.parametrize("rpt", [1, 2, 4, 8])
 @pytest.mark.parametrize("K,N", [(3840, 1000), (15360, 130)])
 def test_two_row_gemv_rows_per_wave(rpt, K, N):
     w4.w4_tune_force("gemv_rows2", rpt)
