@@ -8,6 +8,8 @@ on sampled rows otherwise.  Dequantised tiles must match bit for bit.
 """
 from __future__ import annotations
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -927,6 +929,19 @@ def test_moe_gemm2_pair_equals_two_launches():
             rows.extend(range(row_start[e], row_start[e + 1]))
             rs_v.append(len(rows))
         check_moe_groups(yv1[rows], x1[rows], pools[0], rs_v, [ids[e] for e in keep])
+    # a FC with N = 0 touches none of its buffers: the pair equals the other FC's own
+    # launch (torch hands out NULL for empty tensors, so the C-ABI is called directly)
+    y1.fill_(0.5)
+    y2.fill_(0.25)
+    ptr = lambda t: t.data_ptr()
+    f1 = w4.MoeGemmFc(ptr(xt1), ptr(dev[0]["qw"]), ptr(dev[0]["s"]), ptr(y1), K1, N1)
+    f0 = w4.MoeGemmFc(ptr(xt2), ptr(dev[1]["qw"]), ptr(dev[1]["s"]), ptr(y2), K2, 0)
+    stream = torch.cuda.current_stream().cuda_stream
+    assert w4.lib.w4_moe_gemm2(ctypes.byref(f1), ctypes.byref(f0), ptr(rs), ptr(idt), R, len(ids), mr,
+                               si.MOE_POOL, stream) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), r1.view(torch.int16)), "FC1 alone differs from its own launch"
+    assert torch.all(y2 == 0.25), "the FC with N = 0 wrote its output"
 
 
 def test_moe_gemm_row_table_clamped():
