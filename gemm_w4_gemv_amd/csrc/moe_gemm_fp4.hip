@@ -12,7 +12,7 @@
 //     group) x (groups).  A workgroup whose slab starts past its group's last
 //     row exits at once; an expert id outside the pool turns the slab's
 //     outputs into NaN without reading any weight.
-//   * 8 waves split the K range in steps of 128 k; a wave issues and
+//   * 4 waves split the K range in steps of 128 k; a wave issues and
 //     computes exactly its own steps (a wave-uniform exit at the end of its
 //     range).  Per step, lane (i, b) of
 //     a column block loads 16 bytes (words 4b..4b+3, 8 codes per word) of
@@ -27,7 +27,7 @@
 //   * Activations are loaded 4 rows x 256 bytes per instruction and put in
 //     the A layout through a 4 KB LDS tile of the wave's own; the scales of
 //     the workgroup's weight rows are staged in LDS once.
-//   * The 8 waves' partial sums are added through LDS in a fixed order.
+//   * The 4 waves' partial sums are added through LDS in a fixed order.
 #include <type_traits>
 
 #include "w4.h"
@@ -38,7 +38,10 @@ namespace w4 {
 namespace {
 
 constexpr int kStep = 128;  // k per step: 4 MFMA k-slices, 4 scale groups
-constexpr int kWaves = 8, kThreads = kWaves * kWave;
+// Four waves per workgroup: four workgroups (four waves per SIMD) share a
+// compute unit, so a 6 x 16-row pair of FCs starts 1024 of its 1152
+// workgroups at once, and each wave streams a quarter of K.
+constexpr int kWaves = 4, kThreads = kWaves * kWave;
 constexpr int kMaxSteps = W4_MOE_GEMM_MAX_K / kStep;
 
 __device__ __forceinline__ f32x4_t mfma(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
@@ -147,8 +150,7 @@ __device__ __forceinline__ void moe_gemm_tile(const GemmFc& f, const int32_t* __
     };
 
     // Steps of loads in flight per wave: two at 32 rows per workgroup keeps
-    // the kernel within 128 VGPRs, so two workgroups (four waves per SIMD)
-    // share a compute unit.
+    // the kernel within 128 VGPRs (four waves per SIMD).
     constexpr int kSlots = kCB == 2 ? 2 : 4;
     Slot<kCB> ring[kSlots];
 #pragma unroll
@@ -272,10 +274,11 @@ __global__ __launch_bounds__(kThreads) void moe_gemm2_fp4_kernel(GemmFc f1, Gemm
     else moe_gemm_tile<kCB2>(f2, row_start, ids, R, num_experts, blockIdx.x - b1, lds);
 }
 
-// 32 weight rows per workgroup (two workgroups per compute unit) when that
+// 32 weight rows per workgroup (four workgroups per compute unit) when that
 // gives at least 240 workgroups for groups of max_rows rows, else 16.
-// Measured on 6 experts x 16 rows, FC1 and FC2: 26.1 us per pair at 32 rows,
-// 29.3 at 16, 30.4 at 64 (one workgroup per compute unit).
+// Measured on 6 experts x 16 rows, FC1 and FC2 in one launch: 20.3 us per
+// pair at 32 rows, 25.1 at 16, 23.6 at 64 (183 VGPRs: two workgroups per
+// compute unit).
 int column_blocks(int N, int slabs, int E) { return (long)((N + 31) / 32) * slabs * E >= 240 ? 2 : 1; }
 
 }  // namespace
