@@ -890,6 +890,20 @@ def test_moe_gemm_multi_slab_invalid_id_and_untouched_rows():
     check_moe_groups(yv, x, pool, row_start[:4], ids[:3])
 
 
+@pytest.mark.parametrize("K", [128, 384, 640])
+def test_moe_gemm_fewer_steps_than_waves(K):
+    """K split over the workgroup's waves in steps of 128 k with fewer steps than
+    waves (1 or 3) or a ragged split (5): waves with no steps add nothing."""
+    P, N = 5, 80
+    pool = si.fp4_pool(54, (K,), P, K, N)
+    dev_pool = host.fp4_tensors(pool)
+    row_start, ids = [0, 7, 7, 30], [4, 1, 0]  # 7 rows, an empty group, 23 rows (two slabs)
+    x = si.bf16_normal(54, (K, 2), (30, K))
+    print(f"moe_gemm K={K}", flush=True)
+    y = host.bf16_values(run_moe_gemm(dev_pool, x, row_start, ids, 23))
+    check_moe_groups(y, x, pool, row_start, ids)
+
+
 def test_moe_gemm2_pair_equals_two_launches():
     """w4_moe_gemm2: both FC shapes of the 64-expert pools over the same groups
     (6 groups of 16 rows, as bench.py times them, then ragged groups with an empty
