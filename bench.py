@@ -129,6 +129,22 @@ def time_graph(torch, replay, stream, reps: int, warmup: int = 2, trials: int = 
     return sorted(per)[len(per) // 2]
 
 
+# The source pages' own figures, on other GPUs and workloads: context for the
+# numbers above, not a target and not a same-node comparison.
+PAGES_FIGURES = {
+    "note": "the pages' figures on other hardware; context only",
+    "gemma4_decode_step_328_int4_gemvs_ms": {"value": 73, "hardware": "14-SM 10 GB MIG slice",
+                                             "source": "Lab 5: Gemma4 端到端推理优化, 性能分析"},
+    "gemma4_logits_gemv_ms": {"value": 8.67, "hardware": "14-SM 10 GB MIG slice",
+                              "source": "Lab 5: Gemma4 端到端推理优化, 性能分析"},
+    "int4_gemv_eager_us": {"value": 348, "hardware": "14-SM 10 GB MIG slice",
+                           "source": "Lab 5: Gemma4 端到端推理优化, INT4 融合 GEMV"},
+    "fp4_moe_gemm_ms_fallback_cublas_fused": {"value": [52, 14, 6.4], "tok_per_s": [0.79, 1.87],
+                                              "hardware": "SM121 (DGX Spark)",
+                                              "source": "DeepSeek V4 Triton FP4 优化实战, 关键数据"},
+}
+
+
 def floors(w4, torch, stream):
     """Measured ceilings for context: the HBM read rate of a plain streaming read kernel over
     2 GiB (well past the 256 MB MALL), and a graph of 336 empty launches (the launch floor of
@@ -566,6 +582,7 @@ def main() -> int:
         extra.update(extra_workloads(w4, host, si, torch, rf))
     n_lins = len(lins)
     del lins
+    extra["pages_figures_context"] = PAGES_FIGURES
 
     cpu = None
     if not args.no_cpu_baseline:
