@@ -39,7 +39,8 @@ Also reported, outside the timed step:
 
     python bench.py [--steps K] [--warmup W] [--no-extra] [--no-cpu-baseline]
     python bench.py --counters   # only the kernels that HBM counters are read for
-    python bench.py --gemm-calls # only w4_gemm at M = 128 and M = 16 on the two decode shapes, 5 calls each
+    python bench.py --gemm-calls # only w4_gemm at M = 128 and M = 16 on the two decode shapes, 5 calls each,
+                                 # then the grouped FP4 GEMM pair (6 x 16 rows), 5 calls
 
 ``--counters`` runs five chain-kernel launches of the (timed, linked) decode step, then five
 copies of 512 MiB by torch (a plain copy of known size, read once and
@@ -457,6 +458,22 @@ def gemm_calls(w4, torch, host, si) -> int:
                 w4.w4_gemm(x, t["qw"], t["s"], t["z"], y, workspace=ws)
             torch.cuda.synchronize()
             log(f"gemm calls: M={M} K={K} N={N} x5")
+    # the grouped FP4 expert GEMM: 6 experts x 16 rows, FC1 and FC2 in one launch
+    pools = [host.fp4_tensors(p) for p in si.moe_pools()]
+    (K1, N1), (K2, N2) = si.MOE_FC
+    rows = 16
+    R = si.MOE_SLOTS * rows
+    row_start = torch.arange(0, R + 1, rows, dtype=torch.int32, device="cuda")
+    ids = torch.from_numpy(si.moe_inputs(0)[0]).to("cuda")
+    xg1 = host.bf16_tensor(si.bf16_normal(si.SEED, (60, 1), (R, K1)))
+    xg2 = host.bf16_tensor(si.bf16_normal(si.SEED, (60, 2), (R, K2)))
+    yg1 = torch.empty(R, N1, dtype=torch.bfloat16, device="cuda")
+    yg2 = torch.empty(R, N2, dtype=torch.bfloat16, device="cuda")
+    for _ in range(5):
+        w4.w4_moe_gemm2((xg1, pools[0]["qw"], pools[0]["s"], yg1), (xg2, pools[1]["qw"], pools[1]["s"], yg2),
+                        row_start, ids, rows)
+    torch.cuda.synchronize()
+    log(f"moe_gemm2 calls: {si.MOE_SLOTS} groups x {rows} rows, K{K1}->N{N1} and K{K2}->N{N2} x5")
     return 0
 
 
